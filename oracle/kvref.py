@@ -1,0 +1,213 @@
+"""fp64 CPU oracle for one paged GQA decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The HIP library never calls it and it
+never calls the HIP library: the two share no code.
+
+What is computed, and where it comes from:
+
+* Work queue -- the PersistentKV summary (aissential.tech, "PersistentKV:
+  Page-Aware Decode Scheduling ...", Summary and Method) says the engine runs
+  a compact workqueue holding only non-empty (sequence, KV head, sequence
+  split) tasks.  ``build_queue`` enumerates them in (sequence, KV head, split)
+  order with fixed ``split_tokens``-token splits.
+* Page-table gather -- same page (Summary: native page tables; Method: work
+  mapped by KV-head group).  The K/V pool is ``[num_pages, Hkv, P, d]``
+  row-major; logical token ``t`` of sequence ``b`` lives in physical page
+  ``block_tables[b, t // P]`` at slot ``t % P``.
+* Attention -- grouped-query attention: query head ``h`` reads KV head
+  ``h // (Hq // Hkv)``.  The oracle evaluates the plain softmax definition
+  over the whole context (no splitting, no online softmax): split-KV with a
+  log-sum-exp merge reaches the same value up to rounding.
+* Page mass -- the per-page sum of the softmax weights of the step, the
+  page-level attention signal that GrowPage's page budgeting consumes
+  (mlsanity.com GrowPage entry, Abstract: page-level KV abstraction).
+* Query summaries -- GrowPage (Abstract; aitrending.vip article, Technical
+  Details) keeps dual-timescale query summaries.  Here: per (sequence, KV
+  group) a fast and a slow exponential moving average of the group-mean query,
+  ``s <- (1 - a) * s + a * qbar``, and per page the largest scaled dot product
+  of each updated summary with the page's keys.
+
+Everything is float64.  Inputs keep the exact stored bits: float16 arrays, or
+uint16 arrays holding bfloat16 bit patterns, are widened exactly.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "widen", "build_queue", "gather_offsets", "logical_rows", "attention",
+    "update_summaries", "summary_page_max", "decode_step",
+]
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored float16 / bfloat16 (uint16 bits) data."""
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def build_queue(ctx_lens, Hkv: int, split_tokens: int):
+    """Compact task queue (PersistentKV summary, Summary and Method).
+
+    Returns ``tasks`` int32 [n, 4] with rows (seq, kv_head, tok_begin,
+    tok_end), ``group_offsets`` int32 [B*Hkv + 1] (first task of each
+    (seq, kv_head) pair; the last entry is n) and ``n``.
+    A sequence with no tokens contributes no task.
+    """
+    tasks = []
+    offsets = []
+    for b, ctx in enumerate(int(c) for c in ctx_lens):
+        for g in range(Hkv):
+            offsets.append(len(tasks))
+            begin = 0
+            while begin < ctx:
+                end = min(ctx, begin + split_tokens)
+                tasks.append((b, g, begin, end))
+                begin = end
+    offsets.append(len(tasks))
+    arr = np.array(tasks, dtype=np.int32).reshape(-1, 4)
+    return arr, np.array(offsets, dtype=np.int32), len(tasks)
+
+
+def gather_offsets(block_tables, tasks, Hkv: int, page_size: int, d: int, split_tokens: int):
+    """Element offset into the K (or V) pool of every token a task reads.
+
+    Row ``i`` slot ``j`` is the offset of token ``tok_begin + j`` of task ``i``
+    (first element of its d-vector), or -1 when that token is past
+    ``tok_end``.  The pool is ``[num_pages, Hkv, P, d]`` row-major.
+    """
+    n = len(tasks)
+    out = np.full((n, split_tokens), -1, dtype=np.int64)
+    for i in range(n):
+        b, g, t0, t1 = (int(v) for v in tasks[i])
+        for j in range(t1 - t0):
+            t = t0 + j
+            page = int(block_tables[b, t // page_size])
+            out[i, j] = ((page * Hkv + g) * page_size + t % page_size) * d
+    return out
+
+
+def logical_rows(pool, block_tables, b: int, g: int, ctx: int, page_size: int, dtype: str):
+    """The ``ctx`` K (or V) rows of (sequence b, KV head g) in logical order, fp64."""
+    npages = -(-ctx // page_size)
+    pages = np.asarray(block_tables[b, :npages], dtype=np.int64)
+    tiles = pool[pages, g]                      # [npages, P, d], stored type
+    d = tiles.shape[-1]
+    return widen(tiles.reshape(npages * page_size, d)[:ctx], dtype)
+
+
+def attention(q, k_pool, v_pool, block_tables, ctx_lens, page_size: int, scale: float,
+              dtype: str, rows=None):
+    """Softmax attention of each query head over its sequence's cached tokens.
+
+    Returns ``out`` [B, Hq, d], ``lse`` [B, Hq] (natural log of the sum of
+    exp(scaled score)), ``mass`` [B, Hq, max_pages] (softmax weight summed
+    over each logical page; 0 past the last page).  ``rows``: optional
+    iterable of (b, h) to compute; other entries stay NaN.
+    A sequence with no tokens gets out = 0, lse = -inf, mass = 0.
+    """
+    B, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    max_pages = block_tables.shape[1]
+    out = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    mass = np.full((B, Hq, max_pages), np.nan)
+    want = {}
+    for b, h in (rows if rows is not None else ((b, h) for b in range(B) for h in range(Hq))):
+        want.setdefault((int(b), int(h) // G), []).append(int(h))
+    for (b, g), heads in sorted(want.items()):
+        ctx = int(ctx_lens[b])
+        npages = -(-ctx // page_size)
+        if ctx == 0:
+            for h in heads:
+                out[b, h] = 0.0
+                lse[b, h] = -np.inf
+                mass[b, h] = 0.0
+            continue
+        K = logical_rows(k_pool, block_tables, b, g, ctx, page_size, dtype)
+        V = logical_rows(v_pool, block_tables, b, g, ctx, page_size, dtype)
+        for h in heads:
+            qh = widen(q[b, h], dtype)
+            x = scale * (K @ qh)                 # scaled scores, [ctx]
+            M = np.max(x)
+            w = np.exp(x - M)
+            L = np.sum(w)
+            out[b, h] = (w @ V) / L
+            lse[b, h] = M + math.log(L)
+            p = np.zeros(npages * page_size)
+            p[:ctx] = w / L
+            mass[b, h] = 0.0
+            mass[b, h, :npages] = p.reshape(npages, page_size).sum(axis=1)
+    return out, lse, mass
+
+
+def update_summaries(q, s_prev, Hkv: int, alpha_fast: float, alpha_slow: float, dtype: str):
+    """One EMA step of the fast and slow query summaries (GrowPage, Abstract).
+
+    ``qbar`` is the mean of the raw query vectors of the G heads sharing a KV
+    head; each summary moves ``s <- (1 - a) * s + a * qbar``.  ``s_prev`` is
+    [2, B, Hkv, d] (0 = fast, 1 = slow); returns float64 of the same shape.
+    """
+    B, Hq, d = q.shape
+    G = Hq // Hkv
+    qbar = widen(q, dtype).reshape(B, Hkv, G, d).mean(axis=2)
+    s = np.asarray(s_prev, dtype=np.float64)
+    a = np.array([float(np.float32(alpha_fast)), float(np.float32(alpha_slow))], dtype=np.float64)
+    return (1.0 - a)[:, None, None, None] * s + a[:, None, None, None] * qbar[None]
+
+
+def summary_page_max(s_next, k_pool, block_tables, ctx_lens, page_size: int, scale: float,
+                     dtype: str, groups=None):
+    """Per logical page, max over its valid keys of ``scale * (s . k)``.
+
+    For both summaries (fast, slow).  Returns [2, B, Hkv, max_pages]; pages
+    past the sequence's last page hold -inf.  ``groups``: optional iterable
+    of (b, g) to compute; others stay NaN.
+    """
+    _, B, Hkv, d = s_next.shape
+    max_pages = block_tables.shape[1]
+    pm = np.full((2, B, Hkv, max_pages), np.nan)
+    sel = groups if groups is not None else ((b, g) for b in range(B) for g in range(Hkv))
+    for b, g in sel:
+        ctx = int(ctx_lens[b])
+        npages = -(-ctx // page_size)
+        pm[:, b, g] = -np.inf
+        if ctx == 0:
+            continue
+        K = logical_rows(k_pool, block_tables, b, g, ctx, page_size, dtype)
+        for k in range(2):
+            x = np.full(npages * page_size, -np.inf)
+            x[:ctx] = scale * (K @ s_next[k, b, g])
+            pm[k, b, g, :npages] = x.reshape(npages, page_size).max(axis=1)
+    return pm
+
+
+def decode_step(wl, rows=None, q=None, s_prev=None):
+    """Every output of one decode step for a workload-like object.
+
+    ``wl`` needs attributes q, k_pool, v_pool, block_tables, ctx_lens,
+    page_size, scale, dtype, Hkv, split_tokens, d, alpha_fast, alpha_slow,
+    s_prev.  ``rows`` restricts attention/mass to (b, h) pairs and the page
+    max to their (b, g) groups.
+    """
+    q = wl.q if q is None else q
+    s_prev = wl.s_prev if s_prev is None else s_prev
+    tasks, offsets, n = build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
+    out, lse, mass = attention(q, wl.k_pool, wl.v_pool, wl.block_tables, wl.ctx_lens,
+                               wl.page_size, wl.scale, wl.dtype, rows=rows)
+    s_next = update_summaries(q, s_prev, wl.Hkv, wl.alpha_fast, wl.alpha_slow, wl.dtype)
+    G = q.shape[1] // wl.Hkv
+    groups = None if rows is None else sorted({(int(b), int(h) // G) for b, h in rows})
+    pm = summary_page_max(s_next, wl.k_pool, wl.block_tables, wl.ctx_lens, wl.page_size,
+                          wl.scale, wl.dtype, groups=groups)
+    return {"tasks": tasks, "group_offsets": offsets, "n_tasks": n, "out": out,
+            "lse": lse, "mass": mass, "s_next": s_next, "page_max": pm}
