@@ -1,0 +1,175 @@
+/*
+ * kvpage.h -- C ABI of libkvpage.so: one decode step of paged grouped-query
+ * attention (GQA) over a block-table KV cache, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * What a step computes (sources are the web pages this library follows):
+ *
+ *   - "PersistentKV: Page-Aware Decode Scheduling for Long-Context LLM
+ *     Serving on Commodity GPUs" (aissential.tech summary), Summary and
+ *     Method: a native block-table decode attention for GQA that reuses each
+ *     K/V tile across the query heads of a KV-head group, reads KV through
+ *     per-sequence page tables, and runs a compact workqueue holding only
+ *     non-empty (sequence, KV head, sequence split) tasks.
+ *   - "GrowPage: On-Demand KV Budgeting for Efficient LLM Reasoning Serving"
+ *     (mlsanity.com entry, Abstract; aitrending.vip article, Technical
+ *     Details): page-level KV budgeting driven by dual-timescale query
+ *     summaries.  The step therefore also emits per-page attention mass and,
+ *     for a fast and a slow summary of each KV group's queries, the largest
+ *     scaled summary-key dot product on every page.
+ *
+ * Problem statement and data layout (every tensor row-major, contiguous):
+ *
+ *   q            [B, Hq, d]                     f16 or bf16 (shape.dtype)
+ *   k_pool       [num_pages, Hkv, P, d]         same dtype; P = page_size
+ *   v_pool       [num_pages, Hkv, P, d]         same dtype
+ *   block_tables int32 [B, max_pages]           logical page -> physical page
+ *   ctx_lens     int32 [B]                      tokens attended by sequence b
+ *   out          [B, Hq, d]                     q's dtype, round to nearest even
+ *   lse          float32 [B, Hq]                natural-log sum of exp(scores)
+ *
+ * Query head h reads KV head h / (Hq / Hkv).  Token t of sequence b is slot
+ * t % P of physical page block_tables[b][t / P].  Scores are
+ * scale * dot(q, k).  A sequence with ctx_lens[b] == 0 has no tasks; its out
+ * rows are 0 and its lse is -inf.
+ *
+ * Ownership and threading: the caller owns every buffer and the stream.
+ * Struct arguments (kvpage_shape, kvpage_budget) are HOST pointers read
+ * during the call; every other pointer is a DEVICE pointer.  Calls enqueue
+ * work on `stream` and return without synchronizing; the library never
+ * allocates, frees or synchronizes and keeps no per-call state.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued;
+ * a failed check returns a negative kvpage_status and enqueues nothing.  A
+ * failed kernel launch returns KVPAGE_ERR_HIP.  Data-dependent preconditions
+ * (0 <= ctx_lens[b] <= max_pages * P, 0 <= block-table entries < num_pages
+ * for the pages a sequence uses) are the caller's: they are not checked, but
+ * every kernel clamps task counts to `capacity` so an inconsistent queue
+ * cannot write past the task arrays.
+ */
+#ifndef KVPAGE_H
+#define KVPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVPAGE_OK = 0,
+  KVPAGE_ERR_INVALID_ARG = -1, /* null pointer, inconsistent or out-of-range shape */
+  KVPAGE_ERR_UNSUPPORTED = -2, /* valid shape this build has no kernel for        */
+  KVPAGE_ERR_CAPACITY = -3,    /* task capacity below kvpage_queue_capacity()     */
+  KVPAGE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed       */
+} kvpage_status;
+
+typedef enum { KVPAGE_F16 = 0, KVPAGE_BF16 = 1 } kvpage_dtype;
+
+/* One queue entry: tokens [tok_begin, tok_end) of KV head kv_head of sequence
+ * seq (PersistentKV summary, Method: row/sequence, KV head, split tasks). */
+typedef struct {
+  int32_t seq, kv_head, tok_begin, tok_end;
+} kvpage_task;
+
+/* Problem shape.  Supported by the kernels: page_size == 16; d in {64, 128};
+ * 1 <= Hq / Hkv <= 8; split_tokens a multiple of page_size in [16, 256];
+ * dtype f16 or bf16; scale finite and > 0.  flags must be 0. */
+typedef struct {
+  int32_t B, Hq, Hkv, d, page_size, split_tokens, max_pages, num_pages;
+  int32_t dtype; /* kvpage_dtype */
+  float scale;   /* usually 1/sqrt(d) */
+  uint32_t flags;
+} kvpage_shape;
+
+/* Budgeting outputs (GrowPage, Abstract: dual-timescale query summaries and
+ * page-level budgeting).  All device pointers, float32, none may be NULL.
+ *   page_mass [B, Hq, max_pages]  softmax weight of each logical page; 0 past
+ *                                 the sequence's last page
+ *   s_prev    [2, B, Hkv, d]      summaries before this step (0 fast, 1 slow)
+ *   s_next    [2, B, Hkv, d]      s <- (1 - a) s + a * mean_h(q); must not
+ *                                 overlap s_prev (swap the two between steps)
+ *   page_max  [2, B, Hkv, max_pages]  max over a page's keys of
+ *                                 scale * dot(s_next, k); -inf past the last page
+ * alpha_fast / alpha_slow in [0, 1] (0.5 and 0.05 in the reference workload). */
+typedef struct {
+  float* page_mass;
+  const float* s_prev;
+  float* s_next;
+  float alpha_fast, alpha_slow;
+  float* page_max;
+} kvpage_budget;
+
+/* Task capacity for `shape`: B * Hkv * ceil(max_pages * page_size /
+ * split_tokens), the most tasks any ctx_lens within max_pages can produce.
+ * Returns a negative kvpage_status for an invalid shape. */
+int32_t kvpage_queue_capacity(const kvpage_shape* shape);
+
+/* Bytes of device workspace kvpage_split_attn / kvpage_merge_splits /
+ * kvpage_page_mass need for `capacity` tasks (split partials: per task and
+ * query head an unnormalised output row, a running max and a running sum).
+ * Negative kvpage_status on error. */
+int64_t kvpage_workspace_bytes(const kvpage_shape* shape, int32_t capacity);
+
+/* Build the compact task queue (PersistentKV summary, Summary: only
+ * non-empty tasks).  For b in order, KV head g in order, split j in order:
+ * one task {b, g, j*S, min(ctx_b, (j+1)*S)} for each j < ceil(ctx_b / S),
+ * S = split_tokens.  Writes tasks[0 .. n), group_offsets[b*Hkv + g] = index
+ * of the first task of (b, g), group_offsets[B*Hkv] = n, and n_tasks[0] = n.
+ * tasks: [capacity]; group_offsets: [B*Hkv + 1]; n_tasks: [1]; all device. */
+int kvpage_build_queue(const kvpage_shape* shape, const int32_t* ctx_lens, kvpage_task* tasks,
+                       int32_t capacity, int32_t* group_offsets, int32_t* n_tasks,
+                       hipStream_t stream);
+
+/* Split attention (PersistentKV summary, Summary/Method: per KV-head group,
+ * each K/V page tile serves all Hq/Hkv query heads).  For every queued task
+ * writes into `workspace` the split partial of each of the group's query
+ * heads: running max, running sum of exponentials and the unnormalised
+ * weighted V row.  With `budget` non-NULL it also writes, for the task's
+ * pages, page_mass relative to the task's own max (finished by
+ * kvpage_page_mass) and the final summary page_max.  budget may be NULL. */
+int kvpage_split_attn(const kvpage_shape* shape, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
+                      const kvpage_task* tasks, const int32_t* n_tasks, int32_t capacity,
+                      void* workspace, const kvpage_budget* budget, hipStream_t stream);
+
+/* Log-sum-exp merge of the split partials of each (sequence, query head),
+ * over its group's task range in split order: out = sum_j w_j o_j / sum_j w_j
+ * l_j with w_j = exp(m_j - max m), lse = max m + ln(sum_j w_j l_j). */
+int kvpage_merge_splits(const kvpage_shape* shape, const int32_t* group_offsets, int32_t capacity,
+                        const void* workspace, void* out, float* lse, hipStream_t stream);
+
+/* kvpage_split_attn followed by kvpage_merge_splits on the same stream. */
+int kvpage_decode_attn(const kvpage_shape* shape, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
+                       const kvpage_task* tasks, const int32_t* group_offsets,
+                       const int32_t* n_tasks, int32_t capacity, void* workspace,
+                       const kvpage_budget* budget, void* out, float* lse, hipStream_t stream);
+
+/* Finish the budgeting outputs after kvpage_decode_attn ran with the same
+ * budget, queue and workspace: page_mass[b,h,p] becomes the softmax weight
+ * of page p (using the merged lse), entries past each sequence's last page
+ * are set (mass 0, page_max -inf), and s_next is written for every (b, g),
+ * including sequences with no tokens. */
+int kvpage_page_mass(const kvpage_shape* shape, const kvpage_budget* budget, const void* q,
+                     const float* lse, const int32_t* ctx_lens, const int32_t* group_offsets,
+                     int32_t capacity, const void* workspace, hipStream_t stream);
+
+/* Test support: the pool element offset each queued task reads for each of
+ * its tokens, computed by the same addressing code as kvpage_split_attn.
+ * offsets: int64 [capacity, split_tokens]; slot j of task i holds the offset
+ * of token tok_begin + j, or -1 past tok_end.  Rows >= n_tasks untouched. */
+int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_tables,
+                                const kvpage_task* tasks, const int32_t* n_tasks,
+                                int32_t capacity, int64_t* offsets, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kvpage_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPAGE_H */

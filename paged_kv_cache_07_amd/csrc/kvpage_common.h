@@ -1,0 +1,72 @@
+// Device-side helpers shared by the kvpage kernels (gfx950 / CDNA4).
+//
+// Addressing follows the paged layout of the PersistentKV summary
+// (aissential.tech, Summary: native page tables): the K and V pools are
+// [num_pages, Hkv, P, d] row-major, so one (page, KV head) tile of P tokens
+// is P*d contiguous elements.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvpage.h"
+
+namespace kvpage {
+
+constexpr int kPage = 16;   // tokens per page: the M dimension of a 16x16 MFMA tile
+constexpr int kWave = 64;   // CDNA wavefront width
+
+// Element offset of the first element of the (physical page, KV head) tile.
+__device__ __forceinline__ int64_t tile_offset(int32_t page, int32_t kv_head, int32_t Hkv,
+                                               int32_t d) {
+  return ((int64_t)page * Hkv + kv_head) * (int64_t)(kPage * d);
+}
+
+// Element offset of logical token t of a sequence whose block-table row is bt_row.
+__device__ __forceinline__ int64_t token_offset(const int32_t* bt_row, int32_t t, int32_t kv_head,
+                                                int32_t Hkv, int32_t d) {
+  return tile_offset(bt_row[t / kPage], kv_head, Hkv, d) + (int64_t)(t % kPage) * d;
+}
+
+// Group-mean query component: heads summed in head order, then scaled by
+// 1/G.  Used by the attention kernel (summary dot products) and by the
+// page-mass kernel (s_next), so both see identical bits.
+template <typename LoadQ>
+__device__ __forceinline__ float group_mean(LoadQ load_q, int G, float inv_g) {
+  float s = load_q(0);
+  for (int h = 1; h < G; ++h) s = __fadd_rn(s, load_q(h));
+  return __fmul_rn(s, inv_g);
+}
+
+// One exponential-moving-average step of a query summary (GrowPage:
+// dual-timescale query summaries): s <- (1 - a) * s + a * qbar, rounded
+// step by step (no contraction) so that every kernel agrees bitwise.
+__device__ __forceinline__ float ema_step(float s_prev, float qbar, float a) {
+  return __fadd_rn(__fmul_rn(__fsub_rn(1.0f, a), s_prev), __fmul_rn(a, qbar));
+}
+
+// Split-partial workspace: for capacity C tasks and G heads per group,
+// o [C][G][D] float (unnormalised), m [C][G] float (running max of the
+// log2-domain score), l [C][G] float (sum of exp2(score - m)).
+struct WorkspaceView {
+  float* o;
+  float* m;
+  float* l;
+};
+
+__host__ __device__ inline size_t ws_o_elems(int64_t cap, int G, int D) { return (size_t)cap * G * D; }
+
+__host__ __device__ inline WorkspaceView ws_view(void* base, int64_t cap, int G, int D) {
+  float* f = reinterpret_cast<float*>(base);
+  WorkspaceView w;
+  w.o = f;
+  w.m = f + ws_o_elems(cap, G, D);
+  w.l = w.m + (size_t)cap * G;
+  return w;
+}
+
+__host__ __device__ inline size_t ws_bytes(int64_t cap, int G, int D) {
+  return ((size_t)cap * G * (D + 2)) * sizeof(float);
+}
+
+}  // namespace kvpage

@@ -1,0 +1,91 @@
+// Compact work-queue builder and the page-table gather exporter.
+//
+// PersistentKV (aissential.tech summary, Summary and Method) schedules a
+// compact workqueue that holds only non-empty (sequence, KV head, sequence
+// split) tasks.  Here one workgroup per sequence computes its first task
+// index from the lengths of the sequences before it (a deterministic prefix
+// sum, no atomics) and writes its Hkv * ceil(ctx / S) tasks coalesced.
+#include "kvpage_common.h"
+
+namespace kvpage {
+
+__device__ __forceinline__ int64_t splits_of(int32_t ctx, int32_t S) {
+  return ctx > 0 ? ((int64_t)ctx + S - 1) / S : 0;
+}
+
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// grid = B workgroups of one wave; workgroup b owns sequence b.
+__global__ void __launch_bounds__(kWave) build_queue_kernel(
+    const int32_t* __restrict__ ctx_lens, int32_t B, int32_t Hkv, int32_t S,
+    kvpage_task* __restrict__ tasks, int32_t capacity, int32_t* __restrict__ group_offsets,
+    int32_t* __restrict__ n_tasks) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  int64_t before = 0;
+  for (int i = lane; i < b; i += kWave) before += splits_of(ctx_lens[i], S);
+  before = wave_sum(before) * Hkv;
+  const int32_t ctx = ctx_lens[b];
+  const int64_t n_b = splits_of(ctx, S);
+  for (int g = lane; g < Hkv; g += kWave) {
+    const int64_t off = before + g * n_b;
+    group_offsets[(int64_t)b * Hkv + g] = (int32_t)(off < capacity ? off : capacity);
+  }
+  const int64_t mine = n_b * Hkv;
+  for (int64_t k = lane; k < mine; k += kWave) {
+    const int64_t idx = before + k;
+    if (idx >= capacity) break;
+    const int32_t g = (int32_t)(k / n_b);
+    const int32_t j = (int32_t)(k % n_b);
+    kvpage_task t;
+    t.seq = b;
+    t.kv_head = g;
+    t.tok_begin = j * S;
+    t.tok_end = min(ctx, (j + 1) * S);
+    tasks[idx] = t;
+  }
+  if (b == B - 1 && lane == 0) {
+    const int64_t total = before + mine;
+    const int32_t clamped = (int32_t)(total < capacity ? total : capacity);
+    group_offsets[(int64_t)B * Hkv] = clamped;
+    n_tasks[0] = clamped;
+  }
+}
+
+// One workgroup per queued task; lane j covers token slots j, j+64, ...
+__global__ void __launch_bounds__(kWave) gather_offsets_kernel(
+    const int32_t* __restrict__ block_tables, int32_t max_pages, int32_t Hkv, int32_t d,
+    int32_t S, const kvpage_task* __restrict__ tasks, const int32_t* __restrict__ n_tasks,
+    int32_t capacity, int64_t* __restrict__ offsets) {
+  const int32_t n = min(n_tasks[0], capacity);
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
+    const kvpage_task t = tasks[i];
+    const int32_t* bt_row = block_tables + (int64_t)t.seq * max_pages;
+    for (int j = threadIdx.x; j < S; j += kWave) {
+      const int32_t tok = t.tok_begin + j;
+      offsets[i * S + j] = tok < t.tok_end ? token_offset(bt_row, tok, t.kv_head, Hkv, d) : -1;
+    }
+  }
+}
+
+hipError_t launch_build_queue(const kvpage_shape& s, const int32_t* ctx_lens, kvpage_task* tasks,
+                              int32_t capacity, int32_t* group_offsets, int32_t* n_tasks,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(build_queue_kernel, dim3(s.B), dim3(kWave), 0, stream, ctx_lens, s.B, s.Hkv,
+                     s.split_tokens, tasks, capacity, group_offsets, n_tasks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_offsets(const kvpage_shape& s, const int32_t* block_tables,
+                                 const kvpage_task* tasks, const int32_t* n_tasks,
+                                 int32_t capacity, int64_t* offsets, hipStream_t stream) {
+  const int grid = capacity < 65536 ? capacity : 65536;
+  hipLaunchKernelGGL(gather_offsets_kernel, dim3(grid), dim3(kWave), 0, stream, block_tables,
+                     s.max_pages, s.Hkv, s.d, s.split_tokens, tasks, n_tasks, capacity, offsets);
+  return hipGetLastError();
+}
+
+}  // namespace kvpage

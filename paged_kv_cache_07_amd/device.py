@@ -1,0 +1,139 @@
+"""Device-resident buffers for one decode step, driven through the C ABI.
+
+Plumbing only: torch allocates device memory and provides the stream; every
+computation is a libkvpage.so kernel called through ``binding``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as K
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def host_to_device(arr: np.ndarray, dtype: str, device):
+    """Upload f16 arrays or bf16 bit patterns (uint16) without changing bits."""
+    torch = _torch()
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device)
+    return t.view(torch.bfloat16)
+
+
+def device_to_bits(t) -> np.ndarray:
+    """Download an f16/bf16 tensor as its raw uint16 bits."""
+    torch = _torch()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DecodeStep:
+    """Inputs, queue, workspace and outputs of one paged GQA decode step.
+
+    ``run()`` enqueues build_queue -> decode_attn (split attention + merge)
+    -> page_mass on torch's current stream.  Summary state double-buffers:
+    each run reads ``s_prev`` and writes ``s_next``; ``swap_summaries()``
+    flips them for the next step.
+    """
+
+    def __init__(self, wl, device="cuda", budget=True, split_tokens=None):
+        torch = _torch()
+        self.wl = wl
+        self.device = torch.device(device)
+        self.split_tokens = split_tokens or wl.split_tokens
+        self.shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, self.split_tokens,
+                                  wl.max_pages, wl.num_pages, wl.dtype, wl.scale)
+        self.capacity = K.kvpage_queue_capacity(self.shape)
+        ws = K.kvpage_workspace_bytes(self.shape, self.capacity)
+        dev = self.device
+        self.q = host_to_device(wl.q, wl.dtype, dev)
+        self.k_pool = host_to_device(wl.k_pool, wl.dtype, dev)
+        self.v_pool = host_to_device(wl.v_pool, wl.dtype, dev)
+        self.block_tables = torch.from_numpy(np.ascontiguousarray(wl.block_tables)).to(dev)
+        self.ctx_lens = torch.from_numpy(np.ascontiguousarray(wl.ctx_lens)).to(dev)
+        self.tasks = torch.zeros((max(1, self.capacity), 4), dtype=torch.int32, device=dev)
+        self.group_offsets = torch.zeros(wl.B * wl.Hkv + 1, dtype=torch.int32, device=dev)
+        self.n_tasks = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.workspace = torch.zeros(max(256, ws), dtype=torch.uint8, device=dev)
+        out_dtype = torch.float16 if wl.dtype == "f16" else torch.bfloat16
+        self.out = torch.zeros((wl.B, wl.Hq, wl.d), dtype=out_dtype, device=dev)
+        self.lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=dev)
+        self.use_budget = budget
+        if budget:
+            self.page_mass = torch.zeros((wl.B, wl.Hq, wl.max_pages), dtype=torch.float32, device=dev)
+            self.page_max = torch.zeros((2, wl.B, wl.Hkv, wl.max_pages), dtype=torch.float32, device=dev)
+            self.s_prev = torch.from_numpy(np.ascontiguousarray(wl.s_prev)).to(dev)
+            self.s_next = torch.zeros_like(self.s_prev)
+            self._make_budget()
+        else:
+            self.budget = None
+
+    def _make_budget(self):
+        self.budget = K.make_budget(self.page_mass, self.s_prev, self.s_next, self.page_max,
+                                    self.wl.alpha_fast, self.wl.alpha_slow)
+
+    def swap_summaries(self):
+        self.s_prev, self.s_next = self.s_next, self.s_prev
+        self._make_budget()
+
+    def set_query(self, q_host: np.ndarray):
+        self.q.copy_(host_to_device(q_host, self.wl.dtype, self.device))
+
+    # -- the three calls of a step --------------------------------------
+    def build_queue(self, stream=None):
+        K.kvpage_build_queue(self.shape, self.ctx_lens, self.tasks, self.capacity,
+                             self.group_offsets, self.n_tasks, stream)
+
+    def decode_attn(self, stream=None):
+        K.kvpage_decode_attn(self.shape, self.q, self.k_pool, self.v_pool, self.block_tables,
+                             self.ctx_lens, self.tasks, self.group_offsets, self.n_tasks,
+                             self.capacity, self.workspace, self.budget, self.out, self.lse, stream)
+
+    def split_attn(self, stream=None):
+        K.kvpage_split_attn(self.shape, self.q, self.k_pool, self.v_pool, self.block_tables,
+                            self.ctx_lens, self.tasks, self.n_tasks, self.capacity,
+                            self.workspace, self.budget, stream)
+
+    def merge_splits(self, stream=None):
+        K.kvpage_merge_splits(self.shape, self.group_offsets, self.capacity, self.workspace,
+                              self.out, self.lse, stream)
+
+    def page_mass_finish(self, stream=None):
+        K.kvpage_page_mass(self.shape, self.budget, self.q, self.lse, self.ctx_lens,
+                           self.group_offsets, self.capacity, self.workspace, stream)
+
+    def run(self, stream=None):
+        self.build_queue(stream)
+        self.decode_attn(stream)
+        if self.use_budget:
+            self.page_mass_finish(stream)
+
+    def gather_offsets(self, stream=None):
+        torch = _torch()
+        offs = torch.full((max(1, self.capacity), self.split_tokens), -7, dtype=torch.int64,
+                          device=self.device)
+        K.kvpage_debug_gather_offsets(self.shape, self.block_tables, self.tasks, self.n_tasks,
+                                      self.capacity, offs, stream)
+        return offs
+
+    def results(self) -> dict:
+        torch = _torch()
+        torch.cuda.synchronize(self.device)
+        n = int(self.n_tasks.item())
+        res = {
+            "n_tasks": n,
+            "tasks": self.tasks[:n].cpu().numpy(),
+            "group_offsets": self.group_offsets.cpu().numpy(),
+            "out_bits": device_to_bits(self.out),
+            "out": self.out.float().cpu().numpy().astype(np.float64),
+            "lse": self.lse.cpu().numpy().astype(np.float64),
+        }
+        if self.use_budget:
+            res["mass"] = self.page_mass.cpu().numpy().astype(np.float64)
+            res["page_max"] = self.page_max.cpu().numpy().astype(np.float64)
+            res["s_next"] = self.s_next.cpu().numpy().astype(np.float64)
+        return res

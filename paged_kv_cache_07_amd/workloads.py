@@ -181,10 +181,10 @@ def _assemble(name, seed, rng, ctx, Hq, Hkv, d, P, S, dtype, num_pages,
     if fill_pools:
         k_pool = _fill_pool(seed, 0, shape, dtype, threads)
         v_pool = _fill_pool(seed, 1, shape, dtype, threads)
-    else:
-        zero = np.float16(0) if dtype == F16 else np.uint16(0)
-        k_pool = np.full(shape, zero)
-        v_pool = np.full(shape, zero)
+    else:  # lengths and tables only (queue-level checks): empty placeholder pools
+        empty = (0, Hkv, P, d)
+        k_pool = np.zeros(empty, dtype=np.float16 if dtype == F16 else np.uint16)
+        v_pool = k_pool.copy()
     return Workload(
         name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, d=d, page_size=P, split_tokens=S,
         dtype=dtype, num_pages=num_pages, ctx_lens=ctx.astype(np.int32), block_tables=bt,
@@ -228,7 +228,7 @@ def make(name: str, seed: int | None = None, ctx_divisor: int = 1, threads=None,
         # B=1, context 32768, 2048 pages scattered over a 4096-page pool.
         ctx = _ctx_scale([32768], ctx_divisor, 16)
         return _assemble(name, seed, rng, ctx, 32, 8, 128, 16, split_tokens, F16,
-                         max(4096 // ctx_divisor, 2 * (-(-ctx[0] // 16)) + 1), **kw)
+                         max(4096 // ctx_divisor, -(-ctx[0] // 16) + 1), **kw)
     if name in ("b8_bimodal", "b8_uniform"):
         if name == "b8_bimodal":
             ctx = np.concatenate([rng.integers(512, 2048 + 1, 4), rng.integers(24576, 65536 + 1, 4)])

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Queue, group offsets and gather offsets bit for bit; attention outputs, page
+mass, summaries and page maxima within the tolerances in gpu_util.  Oracle-
+sized runs compare every output; full-size runs (in the launch configuration
+the benchmark times) compare sampled (sequence, head) rows.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, compare_step, oracle_step, sample_rows, say
+from oracle import kvref
+from paged_kv_cache_07_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_07_amd import binding
+    binding.lib()
+
+
+def _run(wl, budget=True, split_tokens=None, label=""):
+    from paged_kv_cache_07_amd.device import DecodeStep
+    say("run", label or wl.name, "ctx", wl.ctx_lens.tolist()[:8], "G", wl.G, "d", wl.d,
+        wl.dtype, "split", split_tokens or wl.split_tokens, "budget", budget)
+    ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens)
+    ds.run()
+    return ds, ds.results()
+
+
+# ------------------------------------------------------------------ queue ---
+
+@pytest.mark.parametrize("name", W.NAMES)
+def test_queue_bit_exact_full_size(name):
+    wl = W.make(name, fill_pools=False)
+    wl = dataclasses.replace(wl, k_pool=np.zeros((1, wl.Hkv, 16, wl.d), np.float16),
+                             v_pool=np.zeros((1, wl.Hkv, 16, wl.d), np.float16), num_pages=1,
+                             q=np.zeros((wl.B, wl.Hq, wl.d), np.float16), dtype="f16")
+    from paged_kv_cache_07_amd.device import DecodeStep
+    for split in (256, 16, 128):
+        say("queue", name, split)
+        ds = DecodeStep(wl, budget=False, split_tokens=split)
+        ds.build_queue()
+        torch.cuda.synchronize()
+        tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, split)
+        assert int(ds.n_tasks.item()) == n
+        assert np.array_equal(ds.tasks[:n].cpu().numpy(), tasks)
+        assert np.array_equal(ds.group_offsets.cpu().numpy(), offs)
+
+
+@pytest.mark.parametrize("ctx", [[0], [1], [0, 0, 5], [15, 16, 17], [255, 256, 257, 0, 512],
+                                 [4096, 1, 0, 33]])
+def test_queue_edge_lengths(ctx):
+    wl = W.custom(ctx, Hq=8, Hkv=4, d=64, split_tokens=256)
+    from paged_kv_cache_07_amd.device import DecodeStep
+    for split in (16, 32, 256):
+        say("queue-edge", ctx, split)
+        ds = DecodeStep(wl, budget=False, split_tokens=split)
+        ds.build_queue()
+        torch.cuda.synchronize()
+        tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, split)
+        assert int(ds.n_tasks.item()) == n
+        assert np.array_equal(ds.tasks[:n].cpu().numpy(), tasks)
+        assert np.array_equal(ds.group_offsets.cpu().numpy(), offs)
+
+
+# ----------------------------------------------------------- page gather ---
+
+@pytest.mark.parametrize("case", ["tiny16", "tiny256", "edge", "b8_bimodal_small", "b8_zipf_full"])
+def test_gather_offsets_bit_exact(case):
+    from paged_kv_cache_07_amd.device import DecodeStep
+    split = 256
+    if case.startswith("tiny"):
+        wl, split = W.make("tiny"), int(case[4:])
+    elif case == "edge":
+        wl = W.custom([1, 17, 255, 256, 257, 0], Hq=4, Hkv=2, d=64)
+    elif case == "b8_bimodal_small":
+        wl = W.make("b8_bimodal", ctx_divisor=16)
+    else:
+        wl = W.make("b8_zipf", fill_pools=False)
+        kp = np.zeros((1, 8, 16, 128), np.float16)
+        wl = dataclasses.replace(wl, k_pool=kp, v_pool=kp, q=np.zeros((wl.B, wl.Hq, wl.d), np.float16))
+    say("gather", case)
+    ds = DecodeStep(wl, budget=False, split_tokens=split)
+    ds.build_queue()
+    offs = ds.gather_offsets().cpu().numpy()
+    n = int(ds.n_tasks.item())
+    tasks = ds.tasks[:n].cpu().numpy()
+    rows = np.arange(n) if n <= 4096 else np.random.default_rng(1).choice(n, 256, replace=False)
+    want = kvref.gather_offsets(wl.block_tables, tasks[rows], wl.Hkv, wl.page_size, wl.d, split)
+    assert np.array_equal(offs[rows], want)
+
+
+def test_one_hot_query_returns_the_physical_address():
+    """V rows hold their own (page, head, slot); a query singling out one
+    logical token must return that token's physical address through out."""
+    wl = W.custom([37, 100, 300], Hq=8, Hkv=2, d=64, seed=11)
+    P = wl.page_size
+    v = np.zeros(wl.v_pool.shape, dtype=np.float16)
+    pg, hd, sl = np.meshgrid(np.arange(wl.num_pages), np.arange(wl.Hkv), np.arange(P), indexing="ij")
+    v[..., 0], v[..., 1], v[..., 2] = pg, hd, sl
+    rng = np.random.default_rng(0)
+    k = np.zeros(wl.k_pool.shape, dtype=np.float16)
+    q = np.zeros(wl.q.shape, dtype=np.float16)
+    want = {}
+    for b, c in enumerate(wl.ctx_lens):
+        for g in range(wl.Hkv):
+            t = int(rng.integers(0, c))
+            page = wl.block_tables[b, t // P]
+            k[page, g, t % P, g] = 8.0
+            q[b, g * wl.G:(g + 1) * wl.G, g] = 8.0 * np.sqrt(wl.d)
+            want[b, g] = (page, g, t % P)
+    wl2 = dataclasses.replace(wl, k_pool=k, v_pool=v, q=q)
+    _, res = _run(wl2, budget=False, label="one-hot")
+    for (b, g), addr in want.items():
+        for h in range(g * wl.G, (g + 1) * wl.G):
+            np.testing.assert_allclose(res["out"][b, h, :3], addr, rtol=0, atol=0.5)
+
+
+# -------------------------------------------------------------- attention ---
+
+@pytest.mark.parametrize("split", [16, 32, 256])
+def test_tiny_all_outputs(split):
+    wl = W.make("tiny")
+    wl.s_prev = np.random.default_rng(2).standard_normal(wl.s_prev.shape).astype(np.float32)
+    _, res = _run(wl, split_tokens=split, label=f"tiny-S{split}")
+    compare_step(res, oracle_step(wl, split_tokens=split))
+
+
+@pytest.mark.parametrize("name,div", [("b1", 16), ("b8_bimodal", 32), ("b8_uniform", 32),
+                                      ("b8_zipf", 64), ("b64_prefix", 16)])
+def test_oracle_sized_configs_all_outputs(name, div):
+    wl = W.make(name, ctx_divisor=div)
+    _, res = _run(wl, label=f"{name}/{div}")
+    compare_step(res, oracle_step(wl), label=name)
+
+
+@pytest.mark.parametrize("name", ["b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix"])
+def test_full_size_sampled_rows(name):
+    wl = W.make(name)
+    _, res = _run(wl, label=f"{name}-full")
+    rows = sample_rows(wl, 6, seed=3)
+    ref = oracle_step(wl, rows=rows)
+    compare_step(res, ref, label=name)
+    # Properties that hold for every row at any size.
+    mass = res["mass"]
+    for b in range(wl.B):
+        npg = wl.pages_of(b)
+        np.testing.assert_allclose(mass[b, :, :npg].sum(axis=1), 1.0, atol=1e-4)
+        assert np.all(mass[b, :, npg:] == 0)
+        assert np.all(res["page_max"][:, b, :, npg:] == -np.inf)
+        assert np.all(np.isfinite(res["page_max"][:, b, :, :npg]))
+    assert np.all(np.isfinite(res["out"])) and np.all(np.isfinite(res["lse"]))
+
+
+def test_zipf_chained_steps_with_summary_state():
+    """Sixteen decode steps: fresh queries each step, s_next fed back as s_prev."""
+    from paged_kv_cache_07_amd.device import DecodeStep
+    wl = W.make("b8_zipf", ctx_divisor=64)
+    ds = DecodeStep(wl)
+    s_prev = wl.s_prev.astype(np.float64)
+    q = wl.q
+    for step in range(wl.steps):
+        say("zipf-chain step", step)
+        if step:
+            q = W.draw_queries(wl)
+            ds.set_query(q)
+            ds.swap_summaries()
+        ds.run()
+        res = ds.results()
+        ref = oracle_step(wl, q=q, s_prev=s_prev)
+        compare_step(res, ref, label=f"step {step}")
+        s_prev = ref["s_next"]
+
+
+@pytest.mark.parametrize("G,d,dtype", [(1, 128, "f16"), (2, 64, "bf16"), (4, 64, "f16"),
+                                       (8, 128, "bf16"), (8, 64, "f16"), (3, 128, "f16"),
+                                       (5, 128, "bf16")])
+def test_edge_lengths_all_outputs(G, d, dtype):
+    ctx = [0, 1, 15, 16, 17, 255, 256, 257, 1000]
+    wl = W.custom(ctx, Hq=2 * G, Hkv=2, d=d, dtype=dtype, seed=G * 100 + d)
+    wl.s_prev = np.random.default_rng(5).standard_normal(wl.s_prev.shape).astype(np.float32)
+    for split in (16, 256):
+        _, res = _run(wl, split_tokens=split, label=f"edge G{G} d{d} {dtype} S{split}")
+        compare_step(res, oracle_step(wl, split_tokens=split))
+
+
+def test_longest_table_row_is_fully_used():
+    """Context equal to max_pages * P: the last table column is read."""
+    wl = W.custom([16 * 40, 3], Hq=4, Hkv=1, d=128, max_pages=40)
+    _, res = _run(wl, label="max-ctx")
+    compare_step(res, oracle_step(wl))
+
+
+def test_all_sequences_empty():
+    wl = W.custom([0, 0, 0], Hq=4, Hkv=2, d=64)
+    _, res = _run(wl, label="empty")
+    assert res["n_tasks"] == 0
+    assert np.all(res["out"] == 0) and np.all(res["lse"] == -np.inf)
+    assert np.all(res["mass"] == 0) and np.all(res["page_max"] == -np.inf)
+    ref = oracle_step(wl)
+    assert_close("s_next", res["s_next"], ref["s_next"])
+
+
+# -------------------------------------------------------------- robustness ---
+
+def test_nan_poison_in_unreferenced_memory_changes_nothing():
+    for name, div in (("tiny", 1), ("b8_bimodal", 32), ("b64_prefix", 16)):
+        wl = W.make(name, ctx_divisor=div) if div > 1 else W.make(name)
+        _, clean = _run(wl, label=f"{name}-clean")
+        _, dirty = _run(W.poison_unused(wl), label=f"{name}-poisoned")
+        for key in ("out_bits", "lse", "mass", "page_max", "s_next"):
+            assert np.array_equal(clean[key], dirty[key]), (name, key)
+
+
+def test_physical_page_permutation_is_bitwise_invariant():
+    wl = W.make("b8_uniform", ctx_divisor=32)
+    _, base = _run(wl, label="perm-base")
+    pi = np.random.default_rng(9).permutation(wl.num_pages)
+    k = np.empty_like(wl.k_pool)
+    v = np.empty_like(wl.v_pool)
+    k[pi] = wl.k_pool
+    v[pi] = wl.v_pool
+    wl2 = dataclasses.replace(wl, k_pool=k, v_pool=v, block_tables=pi[wl.block_tables].astype(np.int32))
+    _, moved = _run(wl2, label="perm-moved")
+    for key in ("out_bits", "lse", "mass", "page_max", "s_next"):
+        assert np.array_equal(base[key], moved[key]), key
+
+
+def test_repeat_runs_are_bitwise_identical_and_split_calls_match():
+    from paged_kv_cache_07_amd.device import DecodeStep
+    wl = W.make("b8_bimodal", ctx_divisor=16)
+    say("determinism")
+    ds = DecodeStep(wl)
+    ds.run()
+    first = ds.results()
+    ds.run()
+    second = ds.results()
+    for key in ("out_bits", "lse", "mass", "page_max", "s_next"):
+        assert np.array_equal(first[key], second[key]), key
+    # decode_attn == split_attn followed by merge_splits
+    ds.out.zero_()
+    ds.lse.zero_()
+    ds.build_queue()
+    ds.split_attn()
+    ds.merge_splits()
+    ds.page_mass_finish()
+    third = ds.results()
+    for key in ("out_bits", "lse", "mass", "page_max", "s_next"):
+        assert np.array_equal(first[key], third[key]), key
