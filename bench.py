@@ -1,0 +1,221 @@
+"""Benchmark one paged GQA decode step on one MI355X.
+
+A step is the whole hot path on one batch, one kvpage_decode_step call:
+build the task queue, split attention (with the page-mass and query-summary
+budgeting outputs), then the log-sum-exp merge fused with the page-mass /
+summary finish -- three kernels on one stream.  Inputs are seeded synthetic tensors already resident in HBM.  Before
+every timed step the caches are flushed by reading a 1 GiB buffer (outside
+the step's events), so KV bytes come from HBM.
+
+The headline workload is the B1 long-context step (B=1, context 32768,
+Hq=32, Hkv=8, d=128, page 16, fp16, 2048 pages in a 4096-page pool, 256-token
+splits); B8 workloads are reported beside it.
+
+Prints ONE JSON line.  ``value`` is KV bytes read per second over the whole
+step; ``roofline`` rates the split-attention kernel alone (timed with HIP
+events on the stream it runs on) against MI355X's 8 TB/s HBM peak.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "split_attn_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "paged_kv_cache_07_amd", "csrc", "attn.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(config: str):
+    """HBM bytes per split-attention launch from rocprofv3 counters, if they
+    were taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(config)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = True):
+    """Time `steps` whole decode steps of workload `name` (one kvpage_decode_step
+    call each).  Step time: torch events on the launch stream around the call.
+    Attention-kernel time: HIP events recorded by that kernel's own dispatch."""
+    import torch
+
+    from paged_kv_cache_07_amd import binding, workloads as W
+    from paged_kv_cache_07_amd.device import DecodeStep
+
+    wl = W.make(name)
+    ds = DecodeStep(wl, budget=budget)
+    kv = W.kv_bytes(wl)
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    pairs = [(binding.HipEvent(), binding.HipEvent()) for _ in range(steps)]
+    spare = (binding.HipEvent(), binding.HipEvent())
+
+    def one(i):
+        if flush:
+            torch.sum(flush_buf, dim=0, out=sink[0])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0, a1 = pairs[i] if i is not None else spare
+        e0.record(stream)
+        ds.step(opts=binding.make_opts(a0, a1))
+        e1.record(stream)
+        return e0, e1
+
+    for _ in range(warmup):
+        one(None)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for i in range(steps):
+        events.append(one(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in events])
+    attn_ms = np.array([a.elapsed_ms(b) for a, b in pairs])
+    n_tasks = int(ds.n_tasks.item())
+    return {
+        "workload": name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
+        "page_size": wl.page_size, "split_tokens": wl.split_tokens, "dtype": wl.dtype,
+        "ctx_total": int(wl.ctx_lens.sum()), "n_tasks": n_tasks, "kv_bytes": kv,
+        "kv_bytes_unique": W.kv_bytes(wl, unique=True),
+        "step_ms_mean": float(step_ms.mean()), "step_ms_p50": float(np.median(step_ms)),
+        "step_ms_p10": float(np.percentile(step_ms, 10)), "step_ms_p90": float(np.percentile(step_ms, 90)),
+        "attn_ms_mean": float(attn_ms.mean()), "attn_ms_p50": float(np.median(attn_ms)),
+        "wall_s": wall, "cold_cache": flush,
+    }
+
+
+def cpu_baseline(seconds: float = 12.0):
+    """The fp64 oracle on the host: full B1 steps repeated for ~``seconds``."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvref
+    from paged_kv_cache_07_amd import workloads as W
+
+    wl = W.make("b1")
+    kv = W.kv_bytes(wl)
+    n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            kvref.decode_step(wl)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": kv * n / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full B1 steps (ctx 32768, Hq 32, Hkv 8, d 128: queue, attention, "
+                      f"page mass, summaries, page max) in {el:.1f} s, numpy fp64, 1 thread",
+            "steps_per_s": n / el}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="b1")
+    ap.add_argument("--also", default="b8_bimodal,b8_uniform,b8_zipf,b64_prefix",
+                    help="comma-separated extra workloads reported beside the headline one")
+    ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this decode "
+              "step is built and timed on a single MI355X (see the sharding design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from paged_kv_cache_07_amd import binding
+    binding.lib()   # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4}))
+        return
+
+    flush = not args.warm
+    head = time_config(args.config, args.steps, args.warmup, flush)
+    also = {}
+    for name in [x for x in args.also.split(",") if x and x != args.config]:
+        r = time_config(name, max(10, args.steps // 4), max(3, args.warmup // 4), flush)
+        also[name] = {
+            "kv_gbs_step": r["kv_bytes"] / r["step_ms_mean"] / 1e6,
+            "kv_gbs_attn_kernel": r["kv_bytes"] / r["attn_ms_mean"] / 1e6,
+            "frac_hbm_peak_attn": r["kv_bytes"] / r["attn_ms_mean"] / 1e6 / HBM_PEAK_GBS,
+            "steps_per_s": 1e3 / r["step_ms_mean"], "step_ms_mean": r["step_ms_mean"],
+            "attn_ms_mean": r["attn_ms_mean"], "kv_bytes": r["kv_bytes"],
+            "kv_bytes_unique": r["kv_bytes_unique"], "n_tasks": r["n_tasks"], "B": r["B"],
+            "Hq": r["Hq"], "dtype": r["dtype"], "steps": max(10, args.steps // 4),
+        }
+
+    kv = head["kv_bytes"]
+    achieved = kv / head["attn_ms_mean"] / 1e6
+    traffic = measured_traffic(args.config)
+    result = {
+        "metric": "KV GB/s read per decode step (% of HBM peak); decode steps/s at B1 & B8",
+        "value": kv / head["step_ms_mean"] / 1e6,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["step_ms_mean"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic: seeded N(0,1) fp16 q/K/V, pages scattered by a seeded permutation",
+        "config": {"workload": "B1 long-context paged GQA decode step", "B": 1, "context": 32768,
+                   "Hq": 32, "Hkv": 8, "d": 128, "page_size": 16, "split_tokens": 256,
+                   "pool_pages": 4096, "budgeting_outputs": True, "cold_cache": flush},
+        "steps_per_s": 1e3 / head["step_ms_mean"],
+        "frac_hbm_peak_step": kv / head["step_ms_mean"] / 1e6 / HBM_PEAK_GBS,
+        "step_ms_p50": head["step_ms_p50"], "step_ms_p10": head["step_ms_p10"],
+        "step_ms_p90": head["step_ms_p90"], "n_tasks": head["n_tasks"], "kv_bytes": kv,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "split_attn_kernel<128,f16,budget>",
+                     "attn_ms_mean": head["attn_ms_mean"]},
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -108,9 +108,11 @@ typedef struct {
 int32_t kvpage_queue_capacity(const kvpage_shape* shape);
 
 /* Bytes of device workspace kvpage_split_attn / kvpage_merge_splits /
- * kvpage_page_mass need for `capacity` tasks (split partials: per task and
- * query head an unnormalised output row, a running max and a running sum).
- * Negative kvpage_status on error. */
+ * kvpage_page_mass / kvpage_decode_step need for `capacity` tasks: the split
+ * partials (an unnormalised output row, a running max and a running sum per
+ * query head for each run of consecutive tasks of one (sequence, KV head)
+ * that a wavefront processed), the per-task reference of the raw page sums,
+ * and a small header.  Negative kvpage_status on error. */
 int64_t kvpage_workspace_bytes(const kvpage_shape* shape, int32_t capacity);
 
 /* Build the compact task queue (PersistentKV summary, Summary: only
@@ -147,6 +149,30 @@ int kvpage_decode_attn(const kvpage_shape* shape, const void* q, const void* k_p
                        const kvpage_task* tasks, const int32_t* group_offsets,
                        const int32_t* n_tasks, int32_t capacity, void* workspace,
                        const kvpage_budget* budget, void* out, float* lse, hipStream_t stream);
+
+/* Optional launch settings for kvpage_decode_step.
+ *   attn_start / attn_stop: events the split-attention kernel's own dispatch
+ *     records at its start and end (NULL: none).
+ *   max_workgroups: cap on the attention kernel's persistent grid (0: as many
+ *     as are resident on the device).  Fewer workgroups give each wavefront a
+ *     longer contiguous stretch of the queue; results do not depend on it. */
+typedef struct {
+  hipEvent_t attn_start, attn_stop;
+  int32_t max_workgroups;
+} kvpage_launch_opts;
+
+/* One whole decode step in one call, on `stream`: the queue build (as
+ * kvpage_build_queue), split attention (as kvpage_split_attn) and the merge
+ * (as kvpage_merge_splits); with `budget` the merge also finishes the
+ * budgeting outputs exactly as kvpage_page_mass would, in the same kernel.
+ * Outputs equal those of kvpage_build_queue + kvpage_decode_attn (+
+ * kvpage_page_mass).  tasks, group_offsets and n_tasks are written.
+ * opts may be NULL. */
+int kvpage_decode_step(const kvpage_shape* shape, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
+                       kvpage_task* tasks, int32_t* group_offsets, int32_t* n_tasks,
+                       int32_t capacity, void* workspace, const kvpage_budget* budget, void* out,
+                       float* lse, const kvpage_launch_opts* opts, hipStream_t stream);
 
 /* Finish the budgeting outputs after kvpage_decode_attn ran with the same
  * budget, queue and workspace: page_mass[b,h,p] becomes the softmax weight

@@ -42,6 +42,11 @@ class kvpage_budget(ctypes.Structure):
                 ("alpha_slow", ctypes.c_float), ("page_max", ctypes.c_void_p)]
 
 
+class kvpage_launch_opts(ctypes.Structure):
+    _fields_ = [("attn_start", ctypes.c_void_p), ("attn_stop", ctypes.c_void_p),
+                ("max_workgroups", ctypes.c_int32)]
+
+
 class KvpageError(RuntimeError):
     def __init__(self, fn: str, status: int, text: str):
         super().__init__(f"{fn} failed: {status} ({text})")
@@ -60,6 +65,8 @@ _SIGS = {
     "kvpage_decode_attn": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                           _B, _P, _P, _P]),
     "kvpage_page_mass": (ctypes.c_int, [_S, _B, _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
+    "kvpage_decode_step": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                          _B, _P, _P, ctypes.POINTER(kvpage_launch_opts), _P]),
     "kvpage_debug_gather_offsets": (ctypes.c_int, [_S, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "kvpage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -171,8 +178,54 @@ def kvpage_page_mass(shape, budget, q, lse, ctx_lens, group_offsets, capacity, w
         _ptr(ctx_lens), _ptr(group_offsets), capacity, _ptr(workspace), _stream(stream)))
 
 
+def kvpage_decode_step(shape, q, k_pool, v_pool, block_tables, ctx_lens, tasks, group_offsets,
+                       n_tasks, capacity, workspace, budget, out, lse, opts=None, stream=None):
+    return _check("kvpage_decode_step", lib().kvpage_decode_step(
+        ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(ctx_lens), _ptr(tasks), _ptr(group_offsets), _ptr(n_tasks), capacity,
+        _ptr(workspace), None if budget is None else ctypes.byref(budget), _ptr(out), _ptr(lse),
+        None if opts is None else ctypes.byref(opts), _stream(stream)))
+
+
 def kvpage_debug_gather_offsets(shape, block_tables, tasks, n_tasks, capacity, offsets,
                                 stream=None):
     return _check("kvpage_debug_gather_offsets", lib().kvpage_debug_gather_offsets(
         ctypes.byref(shape), _ptr(block_tables), _ptr(tasks), _ptr(n_tasks), capacity,
         _ptr(offsets), _stream(stream)))
+
+
+# ----------------------------------------------------------- HIP events
+# Resolved through libkvpage.so's own dependency scope, so they belong to the
+# same HIP runtime instance as the kernels they time.
+
+class HipEvent:
+    """A HIP event (hipEventCreate) for kernel timestamps."""
+
+    def __init__(self):
+        h = lib()
+        self.handle = ctypes.c_void_p()
+        if h.hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def synchronize(self):
+        if lib().hipEventSynchronize(self.handle) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+
+    def elapsed_ms(self, stop: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        if lib().hipEventElapsedTime(ctypes.byref(ms), self.handle, stop.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            if self.handle:
+                lib().hipEventDestroy(self.handle)
+        except Exception:
+            pass
+
+
+def make_opts(start: HipEvent | None = None, stop: HipEvent | None = None,
+              max_workgroups: int = 0) -> kvpage_launch_opts:
+    return kvpage_launch_opts(start.handle if start else None, stop.handle if stop else None,
+                              max_workgroups)

@@ -13,9 +13,14 @@ hipError_t launch_gather_offsets(const kvpage_shape&, const int32_t*, const kvpa
                                  const int32_t*, int32_t, int64_t*, hipStream_t);
 hipError_t launch_split_attn(const kvpage_shape&, const void*, const void*, const void*,
                              const int32_t*, const kvpage_task*, const int32_t*, int32_t, void*,
-                             const kvpage_budget*, hipStream_t);
+                             const kvpage_budget*, hipStream_t, hipEvent_t, hipEvent_t,
+                             const int32_t*, kvpage_task*, int32_t*, int32_t*, int32_t);
+bool split_attn_can_fuse_queue(const kvpage_shape&);
 hipError_t launch_merge(const kvpage_shape&, const int32_t*, int32_t, const void*, void*, float*,
                         hipStream_t);
+hipError_t launch_merge_finish(const kvpage_shape&, const kvpage_budget&, const void*,
+                               const int32_t*, const int32_t*, int32_t, const void*, void*, float*,
+                               hipStream_t);
 hipError_t launch_page_mass(const kvpage_shape&, const kvpage_budget&, const void*, const float*,
                             const int32_t*, const int32_t*, int32_t, const void*, hipStream_t);
 
@@ -132,7 +137,8 @@ int kvpage_split_attn(const kvpage_shape* s, const void* q, const void* k_pool, 
   if (!ctx_lens) return KVPAGE_ERR_INVALID_ARG;
   if (s->B == 0 || capacity == 0) return KVPAGE_OK;
   return status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks, capacity,
-                                     workspace, budget, stream));
+                                     workspace, budget, stream, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, 0));
 }
 
 int kvpage_merge_splits(const kvpage_shape* s, const int32_t* group_offsets, int32_t capacity,
@@ -156,8 +162,42 @@ int kvpage_decode_attn(const kvpage_shape* s, const void* q, const void* k_pool,
   if (s->B == 0) return KVPAGE_OK;
   if (capacity > 0) {
     KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
-                                       capacity, workspace, budget, stream)));
+                                       capacity, workspace, budget, stream, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr, nullptr, 0)));
   }
+  return status_of(launch_merge(*s, group_offsets, capacity, workspace, out, lse, stream));
+}
+
+int kvpage_decode_step(const kvpage_shape* s, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
+                       kvpage_task* tasks, int32_t* group_offsets, int32_t* n_tasks,
+                       int32_t capacity, void* workspace, const kvpage_budget* budget, void* out,
+                       float* lse, const kvpage_launch_opts* opts, hipStream_t stream) {
+  KV_TRY(validate_attn(s, q, k_pool, v_pool, block_tables, tasks, n_tasks, capacity, workspace,
+                       budget));
+  if (!ctx_lens || !group_offsets || !out || !lse) return KVPAGE_ERR_INVALID_ARG;
+  if (s->B == 0) return KVPAGE_OK;
+  hipEvent_t t0 = opts ? opts->attn_start : nullptr;
+  hipEvent_t t1 = opts ? opts->attn_stop : nullptr;
+  const int max_wg = opts ? opts->max_workgroups : 0;
+  if (max_wg < 0) return KVPAGE_ERR_INVALID_ARG;
+  if (capacity > 0 && split_attn_can_fuse_queue(*s)) {
+    // The attention kernel builds the queue itself (same content, same order).
+    KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
+                                       capacity, workspace, budget, stream, t0, t1, ctx_lens,
+                                       tasks, group_offsets, n_tasks, max_wg)));
+  } else {
+    KV_TRY(status_of(launch_build_queue(*s, ctx_lens, tasks, capacity, group_offsets, n_tasks,
+                                        stream)));
+    if (capacity > 0) {
+      KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
+                                         capacity, workspace, budget, stream, t0, t1, nullptr,
+                                         nullptr, nullptr, nullptr, max_wg)));
+    }
+  }
+  if (budget)
+    return status_of(launch_merge_finish(*s, *budget, q, ctx_lens, group_offsets, capacity,
+                                         workspace, out, lse, stream));
   return status_of(launch_merge(*s, group_offsets, capacity, workspace, out, lse, stream));
 }
 

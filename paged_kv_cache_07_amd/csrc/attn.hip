@@ -13,18 +13,20 @@
 //     3 (bf16) pieces that sum to the float32 summary, so the summary-key dot
 //     products (GrowPage: dual-timescale query summaries) cost no extra pass
 //     over K;
-//   * online softmax keeps, per head, a reference max m in the log2 domain,
-//     moved only when a page's max exceeds it by more than 8 (weights stay
-//     below 2^8 in between);
+//   * a task (at most 16 pages) runs in two passes: all its scores first,
+//     kept in registers, then the weights exp2(score - task max) and P V, so
+//     the partial carries the task's exact max and nothing is rescaled;
 //   * P V comes from 16x16x16 MFMAs whose P operand is the score tile's own
 //     register layout, so no lane shuffles are needed between the two
 //     contractions;
-//   * K/V pages are prefetched DEPTH pages ahead into registers.
+//   * K and V tiles stream through a ring of DEPTH register buffers.
 //
 // Outputs per task go to the workspace: m (log2 domain), l = sum exp2(y - m)
 // and the unnormalised o = sum exp2(y - m) v for each query head of the group.
 #include <float.h>
 #include <math.h>
+
+#include <hip/hip_ext.h>
 
 #include "kvpage_common.h"
 
@@ -86,9 +88,17 @@ struct AttnParams {
   const int32_t* block_tables;
   const kvpage_task* tasks;
   const int32_t* n_tasks;
+  // Fused queue build (one-call step): lengths in, queue arrays out.
+  const int32_t* ctx_lens;
+  kvpage_task* tasks_out;
+  int32_t* group_offsets_out;
+  int32_t* n_tasks_out;
+  int32_t split_tokens;
+  int32_t* ws_hdr;
   float* ws_o;
-  float* ws_m;
-  float* ws_l;
+  float* ws_rm;
+  float* ws_rl;
+  float* ws_tm;
   float* page_mass;
   const float* s_prev;
   float* page_max;
@@ -99,16 +109,28 @@ struct AttnParams {
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kMaxPagesPerTask = 16;
-constexpr float kRescaleLog2 = 8.0f;
 
-__device__ __forceinline__ float row_allreduce_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, kWave));
-  return fmaxf(v, __shfl_xor(v, 32, kWave));
+// All-reduce over the four 16-lane rows of a wavefront (lanes n, n+16, n+32,
+// n+48) with the gfx950 row-swap permutes: after a swap each lane holds its
+// own value and its partner's, in some order.
+__device__ __forceinline__ float rows_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ float row_allreduce_sum(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  return v + __shfl_xor(v, 32, kWave);
+__device__ __forceinline__ float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Value of the lane `k` columns to the right inside the same 16-lane row.
+template <int k>
+__device__ __forceinline__ float from_right(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + k, 0xf, 0xf, true));
 }
 
 // Two 16-bit halves (lo from a, hi from b), picking half `hi_half` of each word.
@@ -116,22 +138,88 @@ __device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, bool hi_ha
   return hi_half ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH>
+// One task = pages [0, npg) of one (sequence, KV head) split, npg <= 16.
+// Pass 1 streams the K tiles and keeps every score (16 pages x 4 values per
+// lane); pass 2 streams the V tiles and applies exp2(score - task max), so
+// the task's max is exact and no accumulator is ever rescaled.  Tile loads
+// form one stream (K pages 0..15, then V pages 0..15) fetched DEPTH tiles
+// ahead; loads are issued for all 32 tiles whatever npg is (indices past
+// npg - 1 repeat the last page) so the compiler can count outstanding loads
+// exactly, while computation past npg is skipped.
+// Task lookup for the fused queue build (at most 64 sequences): lane b holds
+// sequence b's split count and the inclusive prefix of task counts, so the
+// (sequence, KV head, split) of queue position t is one ballot away.  This is
+// the same enumeration as the queue-build kernel.
+struct SeqScan {
+  int ctx, ns, cnt, incl, total;
+};
+
+__device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, int Hkv, int S,
+                                                int lane) {
+  SeqScan q;
+  q.ctx = lane < B ? max(ctx_lens[lane], 0) : 0;
+  q.ns = (q.ctx + S - 1) / S;
+  q.cnt = q.ns * Hkv;
+  int v = q.cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  q.incl = v;
+  q.total = __builtin_amdgcn_readlane(v, kWave - 1);
+  return q;
+}
+
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const AttnParams p) {
   using E = Elem<BF>;
-  constexpr int KB = D / 32;   // 16x16x32 MFMAs per page for Q K^T
+  constexpr int KB = D / 32;   // 16x16x32 MFMAs per page for the scores
   constexpr int VD = D / 16;   // output column blocks; V halves per lane per token
   constexpr int VW = VD / 2;   // V dwords per lane per token
+  constexpr int TW = D / 8;    // dwords per lane per tile (K or V)
   constexpr int NPC = E::kPieces;
+  constexpr int NT = 2 * kMaxPagesPerTask;
+  constexpr int QCL = 8 * D / 8 / kWave;          // 16-byte query chunks per lane (8 rows max)
+  constexpr int kQStage = 8 * D / 2 + 2 * D;      // staging words: 8 query rows, 2 summary rows
+
+  // Per-wave LDS: staged query / summary rows, and the scores of the task.
+  __shared__ uint32_t lds_q[kWavesPerGroup * kQStage];
+  __shared__ f32x4 lds_s[kWavesPerGroup][kMaxPagesPerTask][kWave];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane >> 4;       // row of 16 lanes
   const int n = lane & 15;       // column inside the row
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int first = blockIdx.x * kWavesPerGroup + wave;
-  const int stride = gridDim.x * kWavesPerGroup;
-  const int ntask = min(p.n_tasks[0], p.capacity);
+  const int gw = blockIdx.x * kWavesPerGroup + wave;
+  const int nwaves = gridDim.x * kWavesPerGroup;
+  int ntask;
+  SeqScan sq;
+  if constexpr (FUSEDQ) {
+    sq = scan_lengths(p.ctx_lens, p.B, p.Hkv, p.split_tokens, lane);
+    ntask = min(sq.total, p.capacity);
+    if (blockIdx.x == 0 && wave == 0) {
+      if (lane < p.B) {
+        const int start = sq.incl - sq.cnt;
+        for (int g = 0; g < p.Hkv; ++g)
+          p.group_offsets_out[lane * p.Hkv + g] = min(start + g * sq.ns, p.capacity);
+      }
+      if (lane == 0) {
+        p.group_offsets_out[p.B * p.Hkv] = ntask;
+        p.n_tasks_out[0] = ntask;
+      }
+    }
+  } else {
+    ntask = min(p.n_tasks[0], p.capacity);
+  }
+  // Wave gw runs the contiguous queue range [gw*c, gw*c + c).
+  const int c = max(1, (ntask + nwaves - 1) / nwaves);
+  if (blockIdx.x == 0 && wave == 0 && lane == 0) p.ws_hdr[0] = c;
+  const int t_first = gw * c;
+  const int t_last = min(t_first + c, ntask);   // exclusive
+  if (t_first >= t_last) return;
+
   const int G = p.G;
   const bool is_head = n < G;
   const bool is_sum = BUDGET && n >= G && n < G + 2 * NPC;
@@ -148,161 +236,268 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   const char* kpool = reinterpret_cast<const char*>(p.k_pool);
   const char* vpool = reinterpret_cast<const char*>(p.v_pool);
 
-  for (int t = first; t < ntask; t += stride) {
-    const kvpage_task tk = p.tasks[t];
-    const int b = tk.seq, g = tk.kv_head;
-    const int ntok = tk.tok_end - tk.tok_begin;
-    const int npg = (ntok + kPage - 1) / kPage;
-    const int lp0 = tk.tok_begin / kPage;
-    const int32_t* bt_row = p.block_tables + (int64_t)b * p.max_pages + lp0;
-    const int32_t page_ids = lane < npg ? bt_row[lane] : 0;
-
-    u32x4 kbuf[DEPTH][KB];
-    uint32_t vbuf[DEPTH][4][VW];
-
-    auto load_k = [&](int i, int slot) {
-      const int32_t pid = __builtin_amdgcn_readlane(page_ids, i);
-      const char* base = kpool + tile_offset(pid, g, p.Hkv, D) * 2;
+  struct Task {
+    int t, b, g, tok_begin, tok_end, ntok, npg, lp0;
+  };
+  // Queue entry t: read from the queue, or (fused build) derived from the lengths.
+  auto fetch = [&](int t) {
+    kvpage_task tk;
+    if constexpr (FUSEDQ) {
+      const uint64_t past = __builtin_amdgcn_ballot_w64(sq.incl > t);
+      const int bq = __builtin_ctzll(past);
+      const int start = __builtin_amdgcn_readlane(sq.incl - sq.cnt, bq);
+      const int ns = __builtin_amdgcn_readlane(sq.ns, bq);
+      const int ctx = __builtin_amdgcn_readlane(sq.ctx, bq);
+      const int k = t - start;
+      const int gq = k / ns;
+      const int j = k - gq * ns;
+      tk.seq = bq;
+      tk.kv_head = gq;
+      tk.tok_begin = j * p.split_tokens;
+      tk.tok_end = min(ctx, tk.tok_begin + p.split_tokens);
+    } else {
+      tk = p.tasks[t];
+    }
+    Task k;
+    k.t = t;
+    k.b = tk.seq;
+    k.g = tk.kv_head;
+    k.tok_begin = tk.tok_begin;
+    k.tok_end = tk.tok_end;
+    k.ntok = tk.tok_end - tk.tok_begin;
+    k.npg = (k.ntok + kPage - 1) / kPage;
+    k.lp0 = tk.tok_begin / kPage;
+    return k;
+  };
+  // Lane i < npg holds the physical id of the task's page i.
+  auto load_page_ids = [&](const Task& k) -> int32_t {
+    const int32_t* bt_row = p.block_tables + (int64_t)k.b * p.max_pages + k.lp0;
+    return lane < k.npg ? bt_row[lane] : 0;
+  };
+  // The group's G query rows (contiguous G*D halves) and, when budgeting, its
+  // two summary rows, as compact 16-byte chunks.
+  struct Rows {
+    u32x4 q[QCL];
+    u32x4 s;
+  };
+  auto load_rows = [&](const Task& k) {
+    Rows w;
+    const uint16_t* qblk = p.q + ((int64_t)k.b * p.Hq + (int64_t)k.g * G) * D;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        kbuf[slot][kb] = *reinterpret_cast<const u32x4*>(base + koff[kb]);
-    };
-    auto load_v = [&](int i, int slot) {
-      const int32_t pid = __builtin_amdgcn_readlane(page_ids, i);
-      const char* base = vpool + tile_offset(pid, g, p.Hkv, D) * 2;
+    for (int i = 0; i < QCL; ++i) {
+      const int ch = lane + i * kWave;
+      w.q[i] = ch < G * D / 8 ? *reinterpret_cast<const u32x4*>(qblk + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    }
+    w.s = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (BUDGET) {
+      const int which = lane / (D / 4);
+      const int ch = lane % (D / 4);
+      if (lane < D / 2)
+        w.s = *reinterpret_cast<const u32x4*>(
+            p.s_prev + (((int64_t)which * p.B + k.b) * p.Hkv + k.g) * D + 4 * ch);
+    }
+    return w;
+  };
+  // Tile tau of a task: K page tau for tau < 16, V page tau - 16 after.  Pages
+  // past npg - 1 repeat the last page (the load count never depends on npg).
+  auto load_tile = [&](const Task& k, int32_t ids, int tau, uint32_t (&dst)[TW]) {
+    const bool is_v = tau >= kMaxPagesPerTask;
+    const int pg = min(is_v ? tau - kMaxPagesPerTask : tau, k.npg - 1);
+    const int32_t pid = __builtin_amdgcn_readlane(ids, pg);
+    const int64_t off = tile_offset(pid, k.g, p.Hkv, D) * 2;
+    if (!is_v) {
+      const char* base = kpool + off;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(base + koff[kb]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dst[4 * kb + x] = w[x];
+      }
+    } else {
+      const char* base = vpool + off;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (VW == 4) {
           const u32x4 w = *reinterpret_cast<const u32x4*>(base + voff[e]);
 #pragma unroll
-          for (int x = 0; x < 4; ++x) vbuf[slot][e][x] = w[x];
+          for (int x = 0; x < 4; ++x) dst[VW * e + x] = w[x];
         } else {
           const u32x2 w = *reinterpret_cast<const u32x2*>(base + voff[e]);
 #pragma unroll
-          for (int x = 0; x < VW; ++x) vbuf[slot][e][x] = w[x];
+          for (int x = 0; x < VW; ++x) dst[VW * e + x] = w[x];
         }
       }
-    };
-
-#pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-      if (i < npg) {
-        load_k(i, i);
-        load_v(i, i);
-      }
     }
+  };
 
-    // Column operand: query heads, then summary pieces, then zeros.
-    u32x4 qop[KB];
-    const uint16_t* qrow0 = p.q + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
+  uint32_t* qs = lds_q + wave * kQStage;   // [8][D] halves, then [2][D] floats
+  f32x4* S = lds_s[wave][0];               // page i at S[i * kWave + lane]
+
+  // Column operand from staged rows: query heads, then summary pieces, zeros.
+  auto build_operand = [&](const Rows& rows, u32x4 (&qop)[KB]) {
+#pragma unroll
+    for (int i = 0; i < QCL; ++i) *reinterpret_cast<u32x4*>(qs + 4 * (lane + i * kWave)) = rows.q[i];
+    if constexpr (BUDGET) {
+      if (lane < D / 2) *reinterpret_cast<u32x4*>(qs + 4 * D + 4 * lane) = rows.s;
+    }
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int d0 = 8 * (4 * kb + r);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (is_head) {
-        v = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)n * D + d0);
-      } else if (is_sum) {
+      qop[kb] = is_head ? *reinterpret_cast<const u32x4*>(qs + (n * D + d0) / 2)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (BUDGET) {
+      if (is_sum) {
+        // Group-mean query (heads added in head order), one EMA step, then
+        // pieces in the storage type that sum back to the float32 summary.
         const int which = (n - G) / NPC;
         const int piece = (n - G) % NPC;
         const float a = which ? p.alpha_slow : p.alpha_fast;
-        float acc[8];
+        const float* sp = reinterpret_cast<const float*>(qs + 4 * D) + which * D;
 #pragma unroll
-        for (int h = 0; h < 8; ++h) {
-          if (h < G) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)h * D + d0);
+        for (int kb = 0; kb < KB; ++kb) {
+          const int d0 = 8 * (4 * kb + r);
+          float acc[8];
+          for (int h = 0; h < G; ++h) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(qs + (h * D + d0) / 2);
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
               const float qv = E::value((w[x >> 1] >> (16 * (x & 1))) & 0xffffu);
               acc[x] = h == 0 ? qv : __fadd_rn(acc[x], qv);
             }
           }
-        }
-        const float* sp = p.s_prev + (((int64_t)which * p.B + b) * p.Hkv + g) * D + d0;
-        uint32_t hv[8];
+          uint32_t hv[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float s = ema_step(sp[x], __fmul_rn(acc[x], p.inv_g), a);
-          float rem = s;
-          uint32_t pc = E::bits(rem);
-          for (int k = 0; k < piece; ++k) {
-            rem = __fsub_rn(rem, E::value(pc));
-            pc = E::bits(rem);
+          for (int x = 0; x < 8; ++x) {
+            const float sv = ema_step(sp[d0 + x], __fmul_rn(acc[x], p.inv_g), a);
+            float rem = sv;
+            uint32_t pc = E::bits(rem);
+            for (int k = 0; k < piece; ++k) {
+              rem = __fsub_rn(rem, E::value(pc));
+              pc = E::bits(rem);
+            }
+            hv[x] = pc;
           }
-          hv[x] = pc;
+          u32x4 v;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v[x] = hv[2 * x] | (hv[2 * x + 1] << 16);
+          qop[kb] = v;
         }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = hv[2 * x] | (hv[2 * x + 1] << 16);
       }
-      qop[kb] = v;
     }
+    __builtin_amdgcn_wave_barrier();
+  };
 
-    f32x4 O[VD];
+  Task cur = fetch(t_first);
+  int32_t ids = load_page_ids(cur);
+  Rows rows = load_rows(cur);
+  uint32_t buf[DEPTH][TW];
 #pragma unroll
-    for (int j = 0; j < VD; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mref = is_head ? -INFINITY : INFINITY;  // non-head lanes get zero weights
-    float l = 0.f;
-    float keep[4] = {0.f, 0.f, 0.f, 0.f};         // per-page outputs, page 4*r + u
+  for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
+  u32x4 qop[KB];
+  build_operand(rows, qop);
 
+  // Run state: the running partial of consecutive tasks of one (b, g).
+  int run_start = t_first;
+  float mrun = is_head ? -INFINITY : INFINITY;   // log2-domain reference; non-head lanes weigh 0
+  float l = 0.f;
+  f32x4 O[VD];
+#pragma unroll
+  for (int j = 0; j < VD; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  while (true) {
+    const int b = cur.b, g = cur.g, ntok = cur.ntok, npg = cur.npg, lp0 = cur.lp0;
+
+    // ---- pass 1: scores of every page; page max (budget) and task max ----
+    float keep[4] = {0.f, 0.f, 0.f, 0.f};  // per-page outputs, page 4*r + u
+    float mloc = -INFINITY;                 // in-lane max of this lane's scores
 #pragma unroll
     for (int i = 0; i < kMaxPagesPerTask; ++i) {
+      const int slot = i % DEPTH;
       if (i < npg) {
-        const int slot = i % DEPTH;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = E::mfma_qk(kbuf[slot][kb], qop[kb], acc);
-        if (i + DEPTH < npg) load_k(i + DEPTH, slot);
-
-        // acc[e] = dot(column n, key of token 4r+e).  Summary pieces sit in
-        // adjacent columns: add them into the lead column.
-        float x[4];
+        for (int kb = 0; kb < KB; ++kb) {
+          u32x4 a;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float c = acc[e];
-          if constexpr (BUDGET) {
-            float sum = __fadd_rn(acc[e], __shfl_down(acc[e], 1, 16));
-            if constexpr (NPC == 3) sum = __fadd_rn(sum, __shfl_down(acc[e], 2, 16));
-            c = is_head ? acc[e] : sum;
+          for (int x = 0; x < 4; ++x) a[x] = buf[slot][4 * kb + x];
+          acc = E::mfma_qk(a, qop[kb], acc);
+        }
+        if constexpr (BUDGET) {
+          // Summary pieces sit in adjacent columns: add them into the lead column.
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sum = __fadd_rn(acc[e], from_right<1>(acc[e]));
+            if constexpr (NPC == 3) sum = __fadd_rn(sum, from_right<2>(acc[e]));
+            acc[e] = is_head ? acc[e] : sum;
           }
-          x[e] = c;
         }
         const int nvalid = ntok - kPage * i;
         if (nvalid < kPage) {  // last page is partial: drop slots past the context
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (4 * r + e >= nvalid) {
-              x[e] = -INFINITY;
-#pragma unroll
-              for (int w = 0; w < VW; ++w) vbuf[slot][e][w] = 0u;
-            }
-          }
+          for (int e = 0; e < 4; ++e)
+            if (4 * r + e >= nvalid) acc[e] = -INFINITY;
         }
-        const float pm = row_allreduce_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        const float ymax = pm * p.c2;
-        const bool need = is_head && (ymax > mref + kRescaleLog2);
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float mnew = need ? ymax : mref;
-          const float alpha = need ? (mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mnew)) : 1.f;
-          mref = mnew;
-          l *= alpha;
-          if constexpr (BUDGET) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) keep[u] *= alpha;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ae = __shfl(alpha, 4 * r + e, kWave);
-#pragma unroll
-            for (int j = 0; j < VD; ++j) O[j][e] *= ae;
-          }
+        S[i * kWave + lane] = acc;
+        const float pm = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        if constexpr (BUDGET) {
+          const float pmr = rows_max(pm);
+          mloc = fmaxf(mloc, pmr);
+          if (r == (i >> 2)) keep[i & 3] = pmr * p.scale;  // used by summary lead lanes
+        } else {
+          mloc = fmaxf(mloc, pm);
         }
+      }
+      if (i + DEPTH < NT) load_tile(cur, ids, i + DEPTH, buf[slot]);
+    }
+    // The run's reference moves only when a task's max exceeds it by more
+    // than 8 (log2 domain), so weights stay below 2^8 and rescales are rare.
+    const float ymax = (BUDGET ? mloc : rows_max(mloc)) * p.c2;
+    const bool need = is_head && ymax > mrun + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? (mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - ymax)) : 1.f;
+      mrun = need ? ymax : mrun;
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ae = __shfl(alpha, 4 * r + e, kWave);
+#pragma unroll
+        for (int j = 0; j < VD; ++j) O[j][e] *= ae;
+      }
+    }
+
+    // ---- the next task of this wave (or this one again at the end) ----
+    const int tn = cur.t + 1;
+    const bool has_next = tn < t_last;
+    const Task nxt = fetch(has_next ? tn : cur.t);
+    const int32_t ids_n = load_page_ids(nxt);
+    const Rows rows_n = load_rows(nxt);
+
+    // ---- pass 2: weights, page sums, P V into the run's accumulators ----
+#pragma unroll
+    for (int i = 0; i < kMaxPagesPerTask; ++i) {
+      const int tau = kMaxPagesPerTask + i;
+      const int slot = tau % DEPTH;
+      if (i < npg) {
+        const f32x4 sc = S[i * kWave + lane];
         float pe[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(x[e], p.c2, -mref));
+        for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], p.c2, -mrun));
         const float psum = (pe[0] + pe[1]) + (pe[2] + pe[3]);
         l += psum;
         if constexpr (BUDGET) {
-          const float page_sum = row_allreduce_sum(psum);
-          if (r == (i >> 2)) keep[i & 3] = is_head ? page_sum : pm * p.scale;
+          const float page_sum = rows_sum(psum);
+          if (is_head && r == (i >> 2)) keep[i & 3] = page_sum;
+        }
+        const int nvalid = ntok - kPage * i;
+        if (nvalid < kPage) {  // zero V rows past the context (they may hold NaN)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * r + e >= nvalid) {
+#pragma unroll
+              for (int w = 0; w < VW; ++w) buf[slot][VW * e + w] = 0u;
+            }
         }
         u32x2 pop;
         pop[0] = E::bits(pe[0]) | (E::bits(pe[1]) << 16);
@@ -312,30 +507,42 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           const bool hi = j & 1;
           const int w = j >> 1;
           u32x2 vop;
-          vop[0] = pick_pair(vbuf[slot][0][w], vbuf[slot][1][w], hi);
-          vop[1] = pick_pair(vbuf[slot][2][w], vbuf[slot][3][w], hi);
+          vop[0] = pick_pair(buf[slot][w], buf[slot][VW + w], hi);
+          vop[1] = pick_pair(buf[slot][2 * VW + w], buf[slot][3 * VW + w], hi);
           O[j] = E::mfma_pv(pop, vop, O[j]);
         }
-        if (i + DEPTH < npg) load_v(i + DEPTH, slot);
+      }
+      if (tau + DEPTH < NT) {
+        load_tile(cur, ids, tau + DEPTH, buf[slot]);
+      } else {
+        // The next task's first K tiles; with no next task, the same number of
+        // loads re-read this task's last V tile (just fetched, so cached).
+        const int pg = has_next ? min(tau + DEPTH - NT, nxt.npg - 1) : npg - 1;
+        const int32_t pid = __builtin_amdgcn_readlane(has_next ? ids_n : ids, pg);
+        const char* base = (has_next ? kpool : vpool) + tile_offset(pid, has_next ? nxt.g : g, p.Hkv, D) * 2;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(base + koff[kb]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) buf[slot][4 * kb + x] = w[x];
+        }
       }
     }
 
-    // Task epilogue: partial (m, l, o) per head; per-page budgeting values.
-    const float ltot = row_allreduce_sum(l);
-    if (r == 0 && is_head) {
-      p.ws_m[(int64_t)t * G + n] = mref;
-      p.ws_l[(int64_t)t * G + n] = ltot;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int h = 4 * r + e;
-      if (h < G) {
-        float* dst = p.ws_o + ((int64_t)t * G + h) * D + n * VD;
-#pragma unroll
-        for (int j = 0; j < VD; ++j) dst[j] = O[j][e];
+    // ---- per task: queue entry (fused build) and budgeting values ----
+    const int ti = cur.t;
+    if constexpr (FUSEDQ) {
+      if (lane == 0) {
+        kvpage_task out_t;
+        out_t.seq = b;
+        out_t.kv_head = g;
+        out_t.tok_begin = cur.tok_begin;
+        out_t.tok_end = cur.tok_end;
+        p.tasks_out[ti] = out_t;
       }
     }
     if constexpr (BUDGET) {
+      if (r == 0 && is_head) p.ws_tm[(int64_t)ti * G + n] = mrun;
       float* dst = nullptr;
       if (is_head) {
         dst = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + n) * p.max_pages + lp0;
@@ -349,12 +556,41 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           if (4 * r + u < npg) dst[4 * r + u] = keep[u];
       }
     }
+
+    // ---- run boundary: write the run's partial (m, l, o) per head ----
+    const bool new_group = nxt.b != b || nxt.g != g;
+    if (!has_next || new_group) {
+      const float ltot = rows_sum(l);
+      if (r == 0 && is_head) {
+        p.ws_rm[(int64_t)run_start * G + n] = mrun;
+        p.ws_rl[(int64_t)run_start * G + n] = ltot;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = 4 * r + e;
+        if (h < G) {
+          float* dst = p.ws_o + ((int64_t)run_start * G + h) * D + n * VD;
+#pragma unroll
+          for (int j = 0; j < VD; ++j) dst[j] = O[j][e];
+        }
+      }
+      if (!has_next) break;
+      run_start = tn;
+      mrun = is_head ? -INFINITY : INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int j = 0; j < VD; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      build_operand(rows_n, qop);
+    }
+    cur = nxt;
+    ids = ids_n;
   }
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH>
-static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream) {
-  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH>;
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ>
+static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
+                             hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
+  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ>;
   static int blocks_per_cu[64] = {0};
   static int num_cus[64] = {0};
   int dev = 0;
@@ -373,16 +609,53 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
   }
   const int64_t want = ((int64_t)capacity + kWavesPerGroup - 1) / kWavesPerGroup;
   const int64_t resident = (int64_t)blocks_per_cu[slot] * num_cus[slot];
-  const int grid = (int)(want < resident ? want : resident);
+  int64_t grid64 = want < resident ? want : resident;
+  if (max_wg > 0 && grid64 > max_wg) grid64 = max_wg;
+  const int grid = (int)grid64;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, p);
+  if (ev_start || ev_stop) {
+    // Timestamps taken by the dispatch itself: start and end of this kernel.
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, ev_start,
+                          ev_stop, 0, p);
+  } else {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, p);
+  }
   return hipGetLastError();
 }
+
+// Tiles (4 KiB at d = 128) each wave keeps in flight.
+#ifndef KVPAGE_ATTN_DEPTH
+#define KVPAGE_ATTN_DEPTH 8
+#endif
+
+template <bool FUSEDQ>
+static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
+                           hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                           int max_wg) {
+  constexpr int DP = KVPAGE_ATTN_DEPTH;
+  const bool bf = s.dtype == KVPAGE_BF16;
+  if (s.d == 128) {
+    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                       : launch_one<128, true, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    return bud ? launch_one<128, false, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
+               : launch_one<128, false, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  }
+  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                     : launch_one<64, true, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  return bud ? launch_one<64, false, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
+             : launch_one<64, false, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
+}
+
+// Fused queue build: B <= 64 sequences (one lane each in the task lookup).
+bool split_attn_can_fuse_queue(const kvpage_shape& s) { return s.B >= 1 && s.B <= kWave; }
 
 hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_tables,
                              const kvpage_task* tasks, const int32_t* n_tasks, int32_t capacity,
-                             void* workspace, const kvpage_budget* budget, hipStream_t stream) {
+                             void* workspace, const kvpage_budget* budget, hipStream_t stream,
+                             hipEvent_t ev_start, hipEvent_t ev_stop, const int32_t* ctx_lens,
+                             kvpage_task* tasks_out, int32_t* group_offsets_out,
+                             int32_t* n_tasks_out, int32_t max_wg) {
   const int G = s.Hq / s.Hkv;
   const WorkspaceView ws = ws_view(workspace, capacity, G, s.d);
   AttnParams p;
@@ -392,9 +665,16 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.block_tables = block_tables;
   p.tasks = tasks;
   p.n_tasks = n_tasks;
+  p.ctx_lens = ctx_lens;
+  p.tasks_out = tasks_out;
+  p.group_offsets_out = group_offsets_out;
+  p.n_tasks_out = n_tasks_out;
+  p.split_tokens = s.split_tokens;
+  p.ws_hdr = ws.hdr;
   p.ws_o = ws.o;
-  p.ws_m = ws.m;
-  p.ws_l = ws.l;
+  p.ws_rm = ws.rm;
+  p.ws_rl = ws.rl;
+  p.ws_tm = ws.tm;
   p.page_mass = budget ? budget->page_mass : nullptr;
   p.s_prev = budget ? budget->s_prev : nullptr;
   p.page_max = budget ? budget->page_max : nullptr;
@@ -409,19 +689,10 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.scale = s.scale;
   p.c2 = s.scale * 1.4426950408889634f;
   p.inv_g = 1.0f / (float)G;
-  const bool bf = s.dtype == KVPAGE_BF16;
-  const bool bud = budget != nullptr;
-  constexpr int DP = 4;
-  if (s.d == 128) {
-    if (bf) return bud ? launch_one<128, true, true, DP>(p, capacity, stream)
-                       : launch_one<128, true, false, DP>(p, capacity, stream);
-    return bud ? launch_one<128, false, true, DP>(p, capacity, stream)
-               : launch_one<128, false, false, DP>(p, capacity, stream);
-  }
-  if (bf) return bud ? launch_one<64, true, true, DP>(p, capacity, stream)
-                     : launch_one<64, true, false, DP>(p, capacity, stream);
-  return bud ? launch_one<64, false, true, DP>(p, capacity, stream)
-             : launch_one<64, false, false, DP>(p, capacity, stream);
+  const bool fused = tasks_out != nullptr;
+  if (fused)
+    return dispatch<true>(s, p, capacity, budget != nullptr, stream, ev_start, ev_stop, max_wg);
+  return dispatch<false>(s, p, capacity, budget != nullptr, stream, ev_start, ev_stop, max_wg);
 }
 
 }  // namespace kvpage

@@ -45,28 +45,46 @@ __device__ __forceinline__ float ema_step(float s_prev, float qbar, float a) {
   return __fadd_rn(__fmul_rn(__fsub_rn(1.0f, a), s_prev), __fmul_rn(a, qbar));
 }
 
-// Split-partial workspace: for capacity C tasks and G heads per group,
-// o [C][G][D] float (unnormalised), m [C][G] float (running max of the
-// log2-domain score), l [C][G] float (sum of exp2(score - m)).
+// Workspace.  A header word holds the run length c the attention kernel
+// used: wave w took queue positions [w*c, (w+1)*c) and folded consecutive
+// tasks of one (sequence, KV head) into a single partial, stored at the
+// position of the run's first task.  For capacity C tasks and G heads:
+//   hdr [64]         int32, hdr[0] = c
+//   o   [C][G][D]    float, unnormalised run partial (valid at run starts)
+//   rm  [C][G]       float, run reference max (log2 domain)
+//   rl  [C][G]       float, run sum of exp2(score - rm)
+//   tm  [C][G]       float, per task: the reference its raw page sums use
 struct WorkspaceView {
+  int32_t* hdr;
   float* o;
-  float* m;
-  float* l;
+  float* rm;
+  float* rl;
+  float* tm;
 };
 
-__host__ __device__ inline size_t ws_o_elems(int64_t cap, int G, int D) { return (size_t)cap * G * D; }
+constexpr int kWsHeaderWords = 64;
 
 __host__ __device__ inline WorkspaceView ws_view(void* base, int64_t cap, int G, int D) {
-  float* f = reinterpret_cast<float*>(base);
   WorkspaceView w;
-  w.o = f;
-  w.m = f + ws_o_elems(cap, G, D);
-  w.l = w.m + (size_t)cap * G;
+  w.hdr = reinterpret_cast<int32_t*>(base);
+  w.o = reinterpret_cast<float*>(base) + kWsHeaderWords;
+  w.rm = w.o + (size_t)cap * G * D;
+  w.rl = w.rm + (size_t)cap * G;
+  w.tm = w.rl + (size_t)cap * G;
   return w;
 }
 
 __host__ __device__ inline size_t ws_bytes(int64_t cap, int G, int D) {
-  return ((size_t)cap * G * (D + 2)) * sizeof(float);
+  return (kWsHeaderWords + (size_t)cap * G * (D + 3)) * sizeof(float);
+}
+
+// Queue positions of the run partials of one (sequence, KV head) whose tasks
+// are [lo, hi), for run length c: lo, then every multiple of c inside.
+__host__ __device__ inline int run_count(int lo, int hi, int c) {
+  return hi <= lo ? 0 : 1 + (hi - 1) / c - lo / c;
+}
+__host__ __device__ inline int run_slot(int lo, int i, int c) {
+  return i == 0 ? lo : (lo / c + i) * c;
 }
 
 }  // namespace kvpage

@@ -14,15 +14,32 @@
 namespace kvpage {
 
 constexpr int kMergeThreads = 256;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct FinishParams {
+  float* page_mass;
+  float* page_max;
+  const float* s_prev;
+  float* s_next;
+  float alpha_fast, alpha_slow;
+  const uint16_t* q;
+  const int32_t* ctx_lens;
+  int32_t max_pages, pages_per_split;
+  float inv_g;
+};
 
 struct MergeParams {
   const int32_t* group_offsets;
+  const int32_t* ws_hdr;
   const float* ws_o;
-  const float* ws_m;
-  const float* ws_l;
+  const float* ws_rm;
+  const float* ws_rl;
+  const float* ws_tm;
   uint16_t* out;
   float* lse;
-  int32_t Hq, Hkv, G, capacity;
+  int32_t B, Hq, Hkv, G, capacity;
+  FinishParams fin;
 };
 
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
@@ -45,13 +62,68 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
   else return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// One workgroup per (sequence, query head).
-template <int D, bool BF>
+template <bool BF>
+__device__ __forceinline__ float q_value(const uint16_t* q, int64_t idx) {
+  const uint32_t b16 = q[idx];
+  if constexpr (BF) return __builtin_bit_cast(float, b16 << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)b16);
+}
+
+__device__ __forceinline__ int pages_of(int32_t ctx) {
+  return ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
+}
+
+// Budgeting finish for query head h of sequence b, given its merged lse
+// (natural log, as stored).  Page p of the sequence lies in split
+// p / pages_per_split of the (b, g) task range starting at `lo`; its raw sum
+// (relative to that task's m) becomes the softmax weight of the page.  The
+// workgroup of the group's first head also writes the page-max tails and the
+// next query-summary state of (b, g).
+template <bool BF>
+__device__ void finish_head(const FinishParams& f, const float* ws_tm, int b, int h, int g, int hh,
+                            int B, int Hq, int Hkv, int G, int D, int lo, float lse_nat) {
+  const int npg = pages_of(f.ctx_lens[b]);
+  const float lse2 = lse_nat * kLog2e;
+  float* mrow = f.page_mass + ((int64_t)b * Hq + h) * f.max_pages;
+  for (int pg = threadIdx.x; pg < f.max_pages; pg += kMergeThreads) {
+    float v = 0.f;
+    if (pg < npg) {
+      const int task = lo + pg / f.pages_per_split;
+      v = mrow[pg] * __builtin_amdgcn_exp2f(ws_tm[(int64_t)task * G + hh] - lse2);
+    }
+    mrow[pg] = v;
+  }
+  if (hh != 0) return;
+  for (int k = 0; k < 2; ++k) {
+    float* prow = f.page_max + (((int64_t)k * B + b) * Hkv + g) * f.max_pages;
+    for (int pg = npg + threadIdx.x; pg < f.max_pages; pg += kMergeThreads) prow[pg] = -INFINITY;
+  }
+  const int64_t q0 = ((int64_t)b * Hq + (int64_t)g * G) * D;
+  for (int x = threadIdx.x; x < 2 * D; x += kMergeThreads) {
+    const int which = x >= D;
+    const int d = x - which * D;
+    float acc = q_value<BF>(f.q, q0 + d);
+    for (int hq = 1; hq < G; ++hq) acc = __fadd_rn(acc, q_value<BF>(f.q, q0 + (int64_t)hq * D + d));
+    const int64_t si = (((int64_t)which * B + b) * Hkv + g) * D + d;
+    f.s_next[si] = ema_step(f.s_prev[si], __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
+  }
+}
+
+// One workgroup per (sequence, query head).  With FINISH the budgeting
+// outputs of that head are finished in the same pass.  Thread (r, c) owns
+// output columns 4c..4c+3 and the splits j = r, r + R, ...; it loads U of
+// them at a time (partial row, m and l together, so one memory latency per
+// batch), keeps its own running max, and the threads are combined at the end
+// with the same log-sum-exp rule in a fixed order.
+template <int D, bool BF, bool FINISH>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p) {
-  constexpr int DP = D / 2;                  // float2 columns
-  constexpr int SUB = kMergeThreads / DP;    // splits handled in parallel
-  __shared__ float scratch[kMergeThreads / kWave];
-  __shared__ float2 part[SUB][DP];
+  constexpr int C4 = D / 4;                // float4 columns of one output row
+  constexpr int R = kMergeThreads / C4;    // partial rows read side by side
+  constexpr int U = 16;                    // splits per thread per batch
+  constexpr int NW = kMergeThreads / kWave;
+  __shared__ float scratch[NW];
+  __shared__ float4 part[R][C4];
+  __shared__ float part_m[R], part_l[R];
 
   const int bh = blockIdx.x;
   const int b = bh / p.Hq, h = bh % p.Hq;
@@ -64,136 +136,158 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams 
   if (n <= 0) {
     for (int d = tid; d < D; d += kMergeThreads) orow[d] = 0;
     if (tid == 0) p.lse[bh] = -INFINITY;
+    if constexpr (FINISH)
+      finish_head<BF>(p.fin, p.ws_tm, b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, -INFINITY);
     return;
   }
-  const float* m = p.ws_m + (int64_t)lo * p.G + hh;
-  const float* l = p.ws_l + (int64_t)lo * p.G + hh;
-  float mx = -INFINITY;
-  for (int j = tid; j < n; j += kMergeThreads) mx = fmaxf(mx, m[(int64_t)j * p.G]);
-  const float M = block_reduce(mx, true, scratch);
-  float sl = 0.f;
-  for (int j = tid; j < n; j += kMergeThreads)
-    sl += __builtin_amdgcn_exp2f(m[(int64_t)j * p.G] - M) * l[(int64_t)j * p.G];
-  const float L = block_reduce(sl, false, scratch);
+  const int c = tid % C4, r = tid / C4;
+  // Run partials of this (b, g): queue positions lo, then multiples of the run length.
+  const int runlen = max(1, p.ws_hdr[0]);
+  const int nrun = run_count(lo, hi, runlen);
 
-  const int dp = tid % DP, s = tid / DP;
-  float2 acc = make_float2(0.f, 0.f);
-  const float* o = p.ws_o + ((int64_t)lo * p.G + hh) * D + 2 * dp;
-  for (int j = s; j < n; j += SUB) {
-    const float w = __builtin_amdgcn_exp2f(m[(int64_t)j * p.G] - M);
-    const float2 v = *reinterpret_cast<const float2*>(o + (int64_t)j * p.G * D);
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
+  float tm = -INFINITY, tl = 0.f;               // this thread's running max / sum
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = r; j0 < nrun; j0 += R * U) {
+    float4 v[U];
+    float mv[U], lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * R;
+      if (j < nrun) {
+        const int64_t slot = run_slot(lo, j, runlen);
+        v[u] = *reinterpret_cast<const float4*>(p.ws_o + (slot * p.G + hh) * D + 4 * c);
+        mv[u] = p.ws_rm[slot * p.G + hh];
+        lv[u] = p.ws_rl[slot * p.G + hh];
+      } else {
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        mv[u] = -INFINITY;
+        lv[u] = 0.f;
+      }
+    }
+    float bm = mv[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) bm = fmaxf(bm, mv[u]);
+    const float nm = fmaxf(tm, bm);
+    const float sc = tm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(tm - nm);
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+    tl *= sc;
+    tm = nm;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wu = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u] - nm);
+      acc.x = fmaf(wu, v[u].x, acc.x);
+      acc.y = fmaf(wu, v[u].y, acc.y);
+      acc.z = fmaf(wu, v[u].z, acc.z);
+      acc.w = fmaf(wu, v[u].w, acc.w);
+      tl = fmaf(wu, lv[u], tl);
+    }
   }
-  part[s][dp] = acc;
+  const float M = block_reduce(tm, true, scratch);
+  const float sc = tm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(tm - M);
+  part[r][c] = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+  if (c == 0) {
+    part_m[r] = tm;
+    part_l[r] = tl * sc;
+  }
   __syncthreads();
-  if (s == 0) {
-    float2 t = part[0][dp];
-    for (int i = 1; i < SUB; ++i) {
-      t.x += part[i][dp].x;
-      t.y += part[i][dp].y;
+  float L = 0.f;
+  for (int i = 0; i < R; ++i) L += part_l[i];
+  if (r == 0) {
+    float4 t = part[0][c];
+    for (int i = 1; i < R; ++i) {
+      t.x += part[i][c].x;
+      t.y += part[i][c].y;
+      t.z += part[i][c].z;
+      t.w += part[i][c].w;
     }
     const float inv = 1.0f / L;
-    orow[2 * dp] = to_bits<BF>(t.x * inv);
-    orow[2 * dp + 1] = to_bits<BF>(t.y * inv);
+    const uint32_t w0 = to_bits<BF>(t.x * inv) | ((uint32_t)to_bits<BF>(t.y * inv) << 16);
+    const uint32_t w1 = to_bits<BF>(t.z * inv) | ((uint32_t)to_bits<BF>(t.w * inv) << 16);
+    *reinterpret_cast<uint2*>(orow + 4 * c) = make_uint2(w0, w1);
   }
-  if (tid == 0) p.lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
+  const float lse_nat = (M + log2f(L)) * kLn2;
+  if (tid == 0) p.lse[bh] = lse_nat;
+  if constexpr (FINISH)
+    finish_head<BF>(p.fin, p.ws_tm, b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, lse_nat);
 }
 
-struct MassParams {
-  float* page_mass;
-  float* page_max;
-  const float* s_prev;
-  float* s_next;
-  float alpha_fast, alpha_slow;
-  const uint16_t* q;
-  const float* lse;
-  const int32_t* ctx_lens;
-  const int32_t* group_offsets;
-  const float* ws_m;
-  int32_t B, Hq, Hkv, G, D, max_pages, pages_per_split, capacity;
-  float inv_g;
-  int64_t n_mass, n_pmax, n_state;
-  bool bf;
-};
-
-__device__ __forceinline__ float q_value(const MassParams& p, int64_t idx) {
-  const uint32_t b16 = p.q[idx];
-  if (p.bf) return __builtin_bit_cast(float, b16 << 16);
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)b16);
+// Standalone finish (after a merge already wrote lse): one workgroup per
+// (sequence, query head).
+template <bool BF>
+__global__ void __launch_bounds__(kMergeThreads) finish_kernel(const MergeParams p, int D) {
+  const int bh = blockIdx.x;
+  const int b = bh / p.Hq, h = bh % p.Hq;
+  const int g = h / p.G, hh = h % p.G;
+  const int lo = min(p.group_offsets[b * p.Hkv + g], p.capacity);
+  finish_head<BF>(p.fin, p.ws_tm, b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, p.lse[bh]);
 }
 
-__device__ __forceinline__ int pages_of(int32_t ctx) {
-  return ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
+static MergeParams merge_params(const kvpage_shape& s, const int32_t* group_offsets,
+                                int32_t capacity, const void* workspace, void* out, float* lse,
+                                const kvpage_budget* bud, const void* q, const int32_t* ctx_lens) {
+  const int G = s.Hq / s.Hkv;
+  const WorkspaceView ws = ws_view(const_cast<void*>(workspace), capacity, G, s.d);
+  MergeParams p;
+  p.group_offsets = group_offsets;
+  p.ws_hdr = ws.hdr;
+  p.ws_o = ws.o;
+  p.ws_rm = ws.rm;
+  p.ws_rl = ws.rl;
+  p.ws_tm = ws.tm;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.B = s.B;
+  p.Hq = s.Hq;
+  p.Hkv = s.Hkv;
+  p.G = G;
+  p.capacity = capacity;
+  p.fin.page_mass = bud ? bud->page_mass : nullptr;
+  p.fin.page_max = bud ? bud->page_max : nullptr;
+  p.fin.s_prev = bud ? bud->s_prev : nullptr;
+  p.fin.s_next = bud ? bud->s_next : nullptr;
+  p.fin.alpha_fast = bud ? bud->alpha_fast : 0.f;
+  p.fin.alpha_slow = bud ? bud->alpha_slow : 0.f;
+  p.fin.q = static_cast<const uint16_t*>(q);
+  p.fin.ctx_lens = ctx_lens;
+  p.fin.max_pages = s.max_pages;
+  p.fin.pages_per_split = s.split_tokens / s.page_size;
+  p.fin.inv_g = 1.0f / (float)G;
+  return p;
 }
 
-__global__ void __launch_bounds__(256) page_mass_kernel(const MassParams p) {
-  const int64_t total = p.n_mass + p.n_pmax + p.n_state;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    if (idx < p.n_mass) {
-      const int64_t bh = idx / p.max_pages;
-      const int pg = (int)(idx % p.max_pages);
-      const int b = (int)(bh / p.Hq), h = (int)(bh % p.Hq);
-      const int g = h / p.G, hh = h % p.G;
-      if (pg < pages_of(p.ctx_lens[b])) {
-        const int64_t task = (int64_t)p.group_offsets[b * p.Hkv + g] + pg / p.pages_per_split;
-        float v = 0.f;
-        if (task < p.capacity) {
-          const float e = p.ws_m[task * p.G + hh] - p.lse[bh] * 1.4426950408889634f;
-          v = p.page_mass[idx] * __builtin_amdgcn_exp2f(e);
-        }
-        p.page_mass[idx] = v;
-      } else {
-        p.page_mass[idx] = 0.f;
-      }
-    } else if (idx < p.n_mass + p.n_pmax) {
-      const int64_t k = idx - p.n_mass;
-      const int pg = (int)(k % p.max_pages);
-      const int64_t kbg = k / p.max_pages;
-      const int b = (int)((kbg / p.Hkv) % p.B);
-      if (pg >= pages_of(p.ctx_lens[b])) p.page_max[k] = -INFINITY;
-    } else {
-      const int64_t k = idx - p.n_mass - p.n_pmax;
-      const int d = (int)(k % p.D);
-      const int64_t kbg = k / p.D;
-      const int g = (int)(kbg % p.Hkv);
-      const int b = (int)((kbg / p.Hkv) % p.B);
-      const int which = (int)(kbg / ((int64_t)p.Hkv * p.B));
-      const int64_t q0 = ((int64_t)b * p.Hq + (int64_t)g * p.G) * p.D + d;
-      float acc = q_value(p, q0);
-      for (int h = 1; h < p.G; ++h) acc = __fadd_rn(acc, q_value(p, q0 + (int64_t)h * p.D));
-      const float a = which ? p.alpha_slow : p.alpha_fast;
-      p.s_next[k] = ema_step(p.s_prev[k], __fmul_rn(acc, p.inv_g), a);
-    }
+template <bool FINISH>
+static void launch_merge_variant(const kvpage_shape& s, const MergeParams& p, hipStream_t stream) {
+  const int grid = s.B * s.Hq;
+  const bool bf = s.dtype == KVPAGE_BF16;
+  if (s.d == 128) {
+    if (bf) hipLaunchKernelGGL((merge_kernel<128, true, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
+    else hipLaunchKernelGGL((merge_kernel<128, false, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
+  } else {
+    if (bf) hipLaunchKernelGGL((merge_kernel<64, true, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
+    else hipLaunchKernelGGL((merge_kernel<64, false, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
   }
 }
 
 hipError_t launch_merge(const kvpage_shape& s, const int32_t* group_offsets, int32_t capacity,
                         const void* workspace, void* out, float* lse, hipStream_t stream) {
-  const int G = s.Hq / s.Hkv;
-  const WorkspaceView ws = ws_view(const_cast<void*>(workspace), capacity, G, s.d);
-  MergeParams p;
-  p.group_offsets = group_offsets;
-  p.ws_o = ws.o;
-  p.ws_m = ws.m;
-  p.ws_l = ws.l;
-  p.out = static_cast<uint16_t*>(out);
-  p.lse = lse;
-  p.Hq = s.Hq;
-  p.Hkv = s.Hkv;
-  p.G = G;
-  p.capacity = capacity;
-  const int grid = s.B * s.Hq;
-  if (grid <= 0) return hipSuccess;
-  const bool bf = s.dtype == KVPAGE_BF16;
-  if (s.d == 128) {
-    if (bf) hipLaunchKernelGGL((merge_kernel<128, true>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
-    else hipLaunchKernelGGL((merge_kernel<128, false>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
-  } else {
-    if (bf) hipLaunchKernelGGL((merge_kernel<64, true>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
-    else hipLaunchKernelGGL((merge_kernel<64, false>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
-  }
+  if (s.B * s.Hq <= 0) return hipSuccess;
+  const MergeParams p = merge_params(s, group_offsets, capacity, workspace, out, lse, nullptr,
+                                     nullptr, nullptr);
+  launch_merge_variant<false>(s, p, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_finish(const kvpage_shape& s, const kvpage_budget& bud, const void* q,
+                               const int32_t* ctx_lens, const int32_t* group_offsets,
+                               int32_t capacity, const void* workspace, void* out, float* lse,
+                               hipStream_t stream) {
+  if (s.B * s.Hq <= 0) return hipSuccess;
+  const MergeParams p = merge_params(s, group_offsets, capacity, workspace, out, lse, &bud, q,
+                                     ctx_lens);
+  launch_merge_variant<true>(s, p, stream);
   return hipGetLastError();
 }
 
@@ -201,38 +295,14 @@ hipError_t launch_page_mass(const kvpage_shape& s, const kvpage_budget& bud, con
                             const float* lse, const int32_t* ctx_lens,
                             const int32_t* group_offsets, int32_t capacity, const void* workspace,
                             hipStream_t stream) {
-  const int G = s.Hq / s.Hkv;
-  const WorkspaceView ws = ws_view(const_cast<void*>(workspace), capacity, G, s.d);
-  MassParams p;
-  p.page_mass = bud.page_mass;
-  p.page_max = bud.page_max;
-  p.s_prev = bud.s_prev;
-  p.s_next = bud.s_next;
-  p.alpha_fast = bud.alpha_fast;
-  p.alpha_slow = bud.alpha_slow;
-  p.q = static_cast<const uint16_t*>(q);
-  p.lse = lse;
-  p.ctx_lens = ctx_lens;
-  p.group_offsets = group_offsets;
-  p.ws_m = ws.m;
-  p.B = s.B;
-  p.Hq = s.Hq;
-  p.Hkv = s.Hkv;
-  p.G = G;
-  p.D = s.d;
-  p.max_pages = s.max_pages;
-  p.pages_per_split = s.split_tokens / s.page_size;
-  p.capacity = capacity;
-  p.inv_g = 1.0f / (float)G;
-  p.n_mass = (int64_t)s.B * s.Hq * s.max_pages;
-  p.n_pmax = 2LL * s.B * s.Hkv * s.max_pages;
-  p.n_state = 2LL * s.B * s.Hkv * s.d;
-  p.bf = s.dtype == KVPAGE_BF16;
-  const int64_t total = p.n_mass + p.n_pmax + p.n_state;
-  if (total <= 0) return hipSuccess;
-  int64_t grid = (total + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  hipLaunchKernelGGL(page_mass_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  if (s.B * s.Hq <= 0) return hipSuccess;
+  const MergeParams p = merge_params(s, group_offsets, capacity, workspace, nullptr,
+                                     const_cast<float*>(lse), &bud, q, ctx_lens);
+  const int grid = s.B * s.Hq;
+  if (s.dtype == KVPAGE_BF16)
+    hipLaunchKernelGGL(finish_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d);
+  else
+    hipLaunchKernelGGL(finish_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d);
   return hipGetLastError();
 }
 

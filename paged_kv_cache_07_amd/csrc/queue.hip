@@ -35,17 +35,19 @@ __global__ void __launch_bounds__(kWave) build_queue_kernel(
     group_offsets[(int64_t)b * Hkv + g] = (int32_t)(off < capacity ? off : capacity);
   }
   const int64_t mine = n_b * Hkv;
-  for (int64_t k = lane; k < mine; k += kWave) {
-    const int64_t idx = before + k;
-    if (idx >= capacity) break;
-    const int32_t g = (int32_t)(k / n_b);
-    const int32_t j = (int32_t)(k % n_b);
-    kvpage_task t;
-    t.seq = b;
-    t.kv_head = g;
-    t.tok_begin = j * S;
-    t.tok_end = min(ctx, (j + 1) * S);
-    tasks[idx] = t;
+  // Tasks of (b, g) are contiguous: KV head outer, split inner, lanes over splits.
+  for (int g = 0; g < Hkv; ++g) {
+    const int64_t base = before + g * n_b;
+    for (int j = lane; j < n_b; j += kWave) {
+      const int64_t idx = base + j;
+      if (idx >= capacity) break;
+      kvpage_task t;
+      t.seq = b;
+      t.kv_head = g;
+      t.tok_begin = j * S;
+      t.tok_end = min(ctx, (j + 1) * S);
+      tasks[idx] = t;
+    }
   }
   if (b == B - 1 && lane == 0) {
     const int64_t total = before + mine;

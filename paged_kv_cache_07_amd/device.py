@@ -112,6 +112,13 @@ class DecodeStep:
         if self.use_budget:
             self.page_mass_finish(stream)
 
+    def step(self, opts=None, stream=None):
+        """The whole step in one call (queue, split attention, fused merge+finish)."""
+        K.kvpage_decode_step(self.shape, self.q, self.k_pool, self.v_pool, self.block_tables,
+                             self.ctx_lens, self.tasks, self.group_offsets, self.n_tasks,
+                             self.capacity, self.workspace, self.budget, self.out, self.lse,
+                             opts, stream)
+
     def gather_offsets(self, stream=None):
         torch = _torch()
         offs = torch.full((max(1, self.capacity), self.split_tokens), -7, dtype=torch.int64,

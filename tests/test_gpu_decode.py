@@ -256,3 +256,50 @@ def test_repeat_runs_are_bitwise_identical_and_split_calls_match():
     third = ds.results()
     for key in ("out_bits", "lse", "mass", "page_max", "s_next"):
         assert np.array_equal(first[key], third[key]), key
+
+
+@pytest.mark.parametrize("budget", [True, False])
+def test_one_call_step_equals_separate_calls(budget):
+    """kvpage_decode_step (fused merge + finish, timed attention launch) gives
+    the same bits as kvpage_build_queue + kvpage_decode_attn + kvpage_page_mass."""
+    from paged_kv_cache_07_amd import binding
+    from paged_kv_cache_07_amd.device import DecodeStep
+    for name, div in (("tiny", 1), ("b8_bimodal", 32), ("b64_prefix", 16), ("b8_zipf", 64)):
+        wl = W.make(name, ctx_divisor=div) if div > 1 else W.make(name)
+        wl.s_prev = np.random.default_rng(4).standard_normal(wl.s_prev.shape).astype(np.float32)
+        say("one-call", name, budget)
+        a = DecodeStep(wl, budget=budget)
+        a.run()
+        ra = a.results()
+        b = DecodeStep(wl, budget=budget)
+        start, stop = binding.HipEvent(), binding.HipEvent()
+        b.step(opts=binding.make_opts(start, stop))
+        rb = b.results()
+        stop.synchronize()
+        assert start.elapsed_ms(stop) > 0
+        keys = ["out_bits", "lse", "tasks", "group_offsets"] + (
+            ["mass", "page_max", "s_next"] if budget else [])
+        for key in keys:
+            assert np.array_equal(ra[key], rb[key]), (name, key)
+        if budget:
+            compare_step(rb, oracle_step(wl), label=name)
+
+
+@pytest.mark.parametrize("max_wg", [1, 3])
+def test_long_wave_runs_fold_consecutive_tasks(max_wg):
+    """Few workgroups: each wavefront walks a long stretch of the queue,
+    folding consecutive tasks of one (sequence, KV head) into one partial and
+    crossing group boundaries inside its stretch."""
+    from paged_kv_cache_07_amd import binding
+    from paged_kv_cache_07_amd.device import DecodeStep
+    cases = [W.make("b8_bimodal", ctx_divisor=32), W.make("b64_prefix", ctx_divisor=16),
+             W.custom([0, 1, 300, 17, 1000, 256, 0, 513], Hq=8, Hkv=2, d=128, seed=12),
+             W.custom([700, 33, 2049], Hq=16, Hkv=2, d=64, dtype="bf16", seed=13)]
+    for wl in cases:
+        wl.s_prev = np.random.default_rng(8).standard_normal(wl.s_prev.shape).astype(np.float32)
+        for budget in (True, False):
+            say("long-runs", wl.name, "max_wg", max_wg, "budget", budget)
+            ds = DecodeStep(wl, budget=budget)
+            ds.step(opts=binding.make_opts(max_workgroups=max_wg))
+            res = ds.results()
+            compare_step(res, oracle_step(wl), budget=budget, label=f"{wl.name} wg{max_wg}")
