@@ -98,7 +98,6 @@ struct AttnParams {
   float* ws_o;
   float* ws_rm;
   float* ws_rl;
-  float* ws_tm;
   float* page_mass;
   const float* s_prev;
   float* page_max;
@@ -109,6 +108,7 @@ struct AttnParams {
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kMaxPagesPerTask = 16;
+constexpr int kRunMax = 16;   // most queue positions one wavefront takes in a row
 
 // All-reduce over the four 16-lane rows of a wavefront (lanes n, n+16, n+32,
 // n+48) with the gfx950 row-swap permutes: after a swap each lane holds its
@@ -187,6 +187,13 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   // Per-wave LDS: staged query / summary rows, and the scores of the task.
   __shared__ uint32_t lds_q[kWavesPerGroup * kQStage];
   __shared__ f32x4 lds_s[kWavesPerGroup][kMaxPagesPerTask][kWave];
+  // Per-wave staging of a run's per-task outputs, written out once per run:
+  // raw page sums per head, summary page maxima, the weight reference each
+  // task used, and (fused queue build) the task records.
+  __shared__ float lds_mass[kWavesPerGroup][BUDGET ? kRunMax : 1][8][kPage];
+  __shared__ float lds_pmax[kWavesPerGroup][BUDGET ? kRunMax : 1][2][kPage];
+  __shared__ float lds_tref[kWavesPerGroup][BUDGET ? kRunMax : 1][8];
+  __shared__ kvpage_task lds_task[kWavesPerGroup][FUSEDQ ? kRunMax : 1];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane >> 4;       // row of 16 lanes
@@ -213,12 +220,17 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   } else {
     ntask = min(p.n_tasks[0], p.capacity);
   }
-  // Wave gw runs the contiguous queue range [gw*c, gw*c + c).
-  const int c = max(1, (ntask + nwaves - 1) / nwaves);
+  // The queue is cut into chunks of c consecutive positions (c <= kRunMax,
+  // sized so every wavefront gets nearly the same number of chunks); wave gw
+  // runs chunks gw, gw + nwaves, ...  Run partials start at multiples of c.
+  const int rounds = max(1, (ntask + nwaves * kRunMax - 1) / (nwaves * kRunMax));
+  const int c = max(1, (ntask + nwaves * rounds - 1) / (nwaves * rounds));
+  const int nchunks = (ntask + c - 1) / c;
   if (blockIdx.x == 0 && wave == 0 && lane == 0) p.ws_hdr[0] = c;
-  const int t_first = gw * c;
-  const int t_last = min(t_first + c, ntask);   // exclusive
-  if (t_first >= t_last) return;
+  int chunk = gw;
+  if (chunk >= nchunks) return;
+  int chunk_end = min((chunk + 1) * c, ntask);   // exclusive
+  const int t_first = chunk * c;
 
   const int G = p.G;
   const bool is_head = n < G;
@@ -400,6 +412,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 
   // Run state: the running partial of consecutive tasks of one (b, g).
   int run_start = t_first;
+  int run_lp0 = cur.lp0;
+  int run_pages = 0;
   float mrun = is_head ? -INFINITY : INFINITY;   // log2-domain reference; non-head lanes weigh 0
   float l = 0.f;
   f32x4 O[VD];
@@ -407,7 +421,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   for (int j = 0; j < VD; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   while (true) {
-    const int b = cur.b, g = cur.g, ntok = cur.ntok, npg = cur.npg, lp0 = cur.lp0;
+    const int b = cur.b, g = cur.g, ntok = cur.ntok, npg = cur.npg;
 
     // ---- pass 1: scores of every page; page max (budget) and task max ----
     float keep[4] = {0.f, 0.f, 0.f, 0.f};  // per-page outputs, page 4*r + u
@@ -468,9 +482,11 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     }
 
     // ---- the next task of this wave (or this one again at the end) ----
-    const int tn = cur.t + 1;
-    const bool has_next = tn < t_last;
-    const Task nxt = fetch(has_next ? tn : cur.t);
+    const bool in_chunk = cur.t + 1 < chunk_end;
+    const bool next_chunk = !in_chunk && chunk + nwaves < nchunks;
+    const bool has_next = in_chunk || next_chunk;
+    const int tn = in_chunk ? cur.t + 1 : (next_chunk ? (chunk + nwaves) * c : cur.t);
+    const Task nxt = fetch(tn);
     const int32_t ids_n = load_page_ids(nxt);
     const Rows rows_n = load_rows(nxt);
 
@@ -529,8 +545,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       }
     }
 
-    // ---- per task: queue entry (fused build) and budgeting values ----
-    const int ti = cur.t;
+    // ---- per task: stage the queue entry and budgeting values in LDS ----
+    const int kin = cur.t - run_start;   // position inside the run, < kRunMax
     if constexpr (FUSEDQ) {
       if (lane == 0) {
         kvpage_task out_t;
@@ -538,28 +554,20 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         out_t.kv_head = g;
         out_t.tok_begin = cur.tok_begin;
         out_t.tok_end = cur.tok_end;
-        p.tasks_out[ti] = out_t;
+        lds_task[wave][kin] = out_t;
       }
     }
     if constexpr (BUDGET) {
-      if (r == 0 && is_head) p.ws_tm[(int64_t)ti * G + n] = mrun;
-      float* dst = nullptr;
-      if (is_head) {
-        dst = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + n) * p.max_pages + lp0;
-      } else if (is_lead) {
-        const int which = n == G ? 0 : 1;
-        dst = p.page_max + (((int64_t)which * p.B + b) * p.Hkv + g) * p.max_pages + lp0;
-      }
-      if (dst) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (4 * r + u < npg) dst[4 * r + u] = keep[u];
-      }
+      const f32x4 kv4 = {keep[0], keep[1], keep[2], keep[3]};
+      if (is_head) *reinterpret_cast<f32x4*>(&lds_mass[wave][kin][n][4 * r]) = kv4;
+      if (is_lead) *reinterpret_cast<f32x4*>(&lds_pmax[wave][kin][n == G ? 0 : 1][4 * r]) = kv4;
+      if (r == 0 && is_head) lds_tref[wave][kin][n] = mrun;
     }
+    run_pages += npg;
 
     // ---- run boundary: write the run's partial (m, l, o) per head ----
     const bool new_group = nxt.b != b || nxt.g != g;
-    if (!has_next || new_group) {
+    if (!in_chunk || new_group) {
       const float ltot = rows_sum(l);
       if (r == 0 && is_head) {
         p.ws_rm[(int64_t)run_start * G + n] = mrun;
@@ -574,8 +582,38 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           for (int j = 0; j < VD; ++j) dst[j] = O[j][e];
         }
       }
+      const int nk = kin + 1;
+      if constexpr (FUSEDQ) {
+        __builtin_amdgcn_wave_barrier();
+        if (lane < nk) p.tasks_out[run_start + lane] = lds_task[wave][lane];
+      }
+      if constexpr (BUDGET) {
+        // Raw page sums move to the run's final reference, the one its
+        // partial carries; pages of a run are consecutive in the sequence.
+        __builtin_amdgcn_wave_barrier();
+        for (int h = 0; h < G; ++h) {
+          const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), h));
+          float* row = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0;
+          for (int pp = lane; pp < run_pages; pp += kWave) {
+            const int kk = pp >> 4;
+            row[pp] = lds_mass[wave][kk][h][pp & 15] *
+                      __builtin_amdgcn_exp2f(lds_tref[wave][kk][h] - mh);
+          }
+        }
+        for (int which = 0; which < 2; ++which) {
+          float* row = p.page_max + (((int64_t)which * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0;
+          for (int pp = lane; pp < run_pages; pp += kWave)
+            row[pp] = lds_pmax[wave][pp >> 4][which][pp & 15];
+        }
+      }
       if (!has_next) break;
+      if (next_chunk) {
+        chunk += nwaves;
+        chunk_end = min((chunk + 1) * c, ntask);
+      }
       run_start = tn;
+      run_lp0 = nxt.lp0;
+      run_pages = 0;
       mrun = is_head ? -INFINITY : INFINITY;
       l = 0.f;
 #pragma unroll
@@ -674,7 +712,6 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.ws_o = ws.o;
   p.ws_rm = ws.rm;
   p.ws_rl = ws.rl;
-  p.ws_tm = ws.tm;
   p.page_mass = budget ? budget->page_mass : nullptr;
   p.s_prev = budget ? budget->s_prev : nullptr;
   p.page_max = budget ? budget->page_max : nullptr;

@@ -45,21 +45,21 @@ __device__ __forceinline__ float ema_step(float s_prev, float qbar, float a) {
   return __fadd_rn(__fmul_rn(__fsub_rn(1.0f, a), s_prev), __fmul_rn(a, qbar));
 }
 
-// Workspace.  A header word holds the run length c the attention kernel
-// used: wave w took queue positions [w*c, (w+1)*c) and folded consecutive
-// tasks of one (sequence, KV head) into a single partial, stored at the
-// position of the run's first task.  For capacity C tasks and G heads:
+// Workspace.  A header word holds the chunk length c the attention kernel
+// used: the queue was cut into chunks [k*c, (k+1)*c), each run by one
+// wavefront, which folded consecutive tasks of one (sequence, KV head) into a
+// single partial stored at the position of the run's first task (a chunk
+// start or a group's first task).  For capacity C tasks and G heads:
 //   hdr [64]         int32, hdr[0] = c
 //   o   [C][G][D]    float, unnormalised run partial (valid at run starts)
-//   rm  [C][G]       float, run reference max (log2 domain)
+//   rm  [C][G]       float, run reference max (log2 domain); the raw page
+//                    sums of the run's pages are relative to it as well
 //   rl  [C][G]       float, run sum of exp2(score - rm)
-//   tm  [C][G]       float, per task: the reference its raw page sums use
 struct WorkspaceView {
   int32_t* hdr;
   float* o;
   float* rm;
   float* rl;
-  float* tm;
 };
 
 constexpr int kWsHeaderWords = 64;
@@ -70,12 +70,11 @@ __host__ __device__ inline WorkspaceView ws_view(void* base, int64_t cap, int G,
   w.o = reinterpret_cast<float*>(base) + kWsHeaderWords;
   w.rm = w.o + (size_t)cap * G * D;
   w.rl = w.rm + (size_t)cap * G;
-  w.tm = w.rl + (size_t)cap * G;
   return w;
 }
 
 __host__ __device__ inline size_t ws_bytes(int64_t cap, int G, int D) {
-  return (kWsHeaderWords + (size_t)cap * G * (D + 3)) * sizeof(float);
+  return (kWsHeaderWords + (size_t)cap * G * (D + 2)) * sizeof(float);
 }
 
 // Queue positions of the run partials of one (sequence, KV head) whose tasks
@@ -85,6 +84,11 @@ __host__ __device__ inline int run_count(int lo, int hi, int c) {
 }
 __host__ __device__ inline int run_slot(int lo, int i, int c) {
   return i == 0 ? lo : (lo / c + i) * c;
+}
+// The run start that holds queue position t of a group beginning at lo.
+__host__ __device__ inline int run_of(int lo, int t, int c) {
+  const int s = (t / c) * c;
+  return s > lo ? s : lo;
 }
 
 }  // namespace kvpage

@@ -35,7 +35,6 @@ struct MergeParams {
   const float* ws_o;
   const float* ws_rm;
   const float* ws_rl;
-  const float* ws_tm;
   uint16_t* out;
   float* lse;
   int32_t B, Hq, Hkv, G, capacity;
@@ -80,16 +79,17 @@ __device__ __forceinline__ int pages_of(int32_t ctx) {
 // workgroup of the group's first head also writes the page-max tails and the
 // next query-summary state of (b, g).
 template <bool BF>
-__device__ void finish_head(const FinishParams& f, const float* ws_tm, int b, int h, int g, int hh,
-                            int B, int Hq, int Hkv, int G, int D, int lo, float lse_nat) {
+__device__ void finish_head(const FinishParams& f, const float* ws_rm, int runlen, int b, int h,
+                            int g, int hh, int B, int Hq, int Hkv, int G, int D, int lo,
+                            float lse_nat) {
   const int npg = pages_of(f.ctx_lens[b]);
   const float lse2 = lse_nat * kLog2e;
   float* mrow = f.page_mass + ((int64_t)b * Hq + h) * f.max_pages;
   for (int pg = threadIdx.x; pg < f.max_pages; pg += kMergeThreads) {
     float v = 0.f;
     if (pg < npg) {
-      const int task = lo + pg / f.pages_per_split;
-      v = mrow[pg] * __builtin_amdgcn_exp2f(ws_tm[(int64_t)task * G + hh] - lse2);
+      const int run = run_of(lo, lo + pg / f.pages_per_split, runlen);
+      v = mrow[pg] * __builtin_amdgcn_exp2f(ws_rm[(int64_t)run * G + hh] - lse2);
     }
     mrow[pg] = v;
   }
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams 
     for (int d = tid; d < D; d += kMergeThreads) orow[d] = 0;
     if (tid == 0) p.lse[bh] = -INFINITY;
     if constexpr (FINISH)
-      finish_head<BF>(p.fin, p.ws_tm, b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, -INFINITY);
+      finish_head<BF>(p.fin, p.ws_rm, max(1, p.ws_hdr[0]), b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, -INFINITY);
     return;
   }
   const int c = tid % C4, r = tid / C4;
@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams 
   const float lse_nat = (M + log2f(L)) * kLn2;
   if (tid == 0) p.lse[bh] = lse_nat;
   if constexpr (FINISH)
-    finish_head<BF>(p.fin, p.ws_tm, b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, lse_nat);
+    finish_head<BF>(p.fin, p.ws_rm, max(1, p.ws_hdr[0]), b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, lse_nat);
 }
 
 // Standalone finish (after a merge already wrote lse): one workgroup per
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(kMergeThreads) finish_kernel(const MergeParams
   const int b = bh / p.Hq, h = bh % p.Hq;
   const int g = h / p.G, hh = h % p.G;
   const int lo = min(p.group_offsets[b * p.Hkv + g], p.capacity);
-  finish_head<BF>(p.fin, p.ws_tm, b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, p.lse[bh]);
+  finish_head<BF>(p.fin, p.ws_rm, max(1, p.ws_hdr[0]), b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, p.lse[bh]);
 }
 
 static MergeParams merge_params(const kvpage_shape& s, const int32_t* group_offsets,
@@ -236,7 +236,6 @@ static MergeParams merge_params(const kvpage_shape& s, const int32_t* group_offs
   p.ws_o = ws.o;
   p.ws_rm = ws.rm;
   p.ws_rl = ws.rl;
-  p.ws_tm = ws.tm;
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   p.B = s.B;

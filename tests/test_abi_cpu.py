@@ -42,7 +42,7 @@ def test_capacity_and_workspace_arithmetic():
     s = _shape(B=3, max_pages=7, split_tokens=32)
     assert K.kvpage_queue_capacity(s) == 3 * 8 * 4          # ceil(112 / 32) = 4
     cap = K.kvpage_queue_capacity(s)
-    assert K.kvpage_workspace_bytes(s, cap) == (64 + cap * 4 * (128 + 3)) * 4
+    assert K.kvpage_workspace_bytes(s, cap) == (64 + cap * 4 * (128 + 2)) * 4
 
 
 @pytest.mark.parametrize("kw,status", [
