@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "split_attn_traffic.json")
+TRAFFIC_FILE = os.path.join(PROFILES, "split_attn_traffic.txt")
 ATTN_SRC = os.path.join(ROOT, "paged_kv_cache_07_amd", "csrc", "attn.hip")
 
 
@@ -43,23 +43,36 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(config: str):
-    """HBM bytes per split-attention launch from rocprofv3 counters, if they
-    were taken on the current kernel source (else None)."""
+    """HBM bytes per split-attention launch from rocprofv3 counters (FETCH_SIZE
+    + WRITE_SIZE, scaled by a plain copy), if they were taken on the current
+    kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            data = json.load(f)
-    except (OSError, ValueError):
+            lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    except OSError:
         return None
-    entry = data.get(config)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return entry.get("bytes_per_launch")
+    for parts in lines:
+        if parts[0] != config:
+            continue
+        kv = dict(x.split("=", 1) for x in parts[1:])
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(kv["bytes_per_launch"])
+    return None
 
 
 def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = True):
-    """Time `steps` whole decode steps of workload `name` (one kvpage_decode_step
-    call each).  Step time: torch events on the launch stream around the call.
-    Attention-kernel time: HIP events recorded by that kernel's own dispatch."""
+    """Time workload `name`: one kvpage_decode_step call per step.
+
+    Two timed regions of `steps` steps each, both with the cache flush before
+    every step (outside the timed events):
+      * steps: HIP events (timing-only, no system fence) on the launch stream
+        around each whole step -> step time;
+      * roofline: the split-attention kernel's own dispatch records its start
+        and end (hipExtLaunchKernelGGL events) -> that kernel's duration.
+    They are separate because kernel-level timestamps add a few microseconds
+    to a step.
+    """
     import torch
 
     from paged_kv_cache_07_amd import binding, workloads as W
@@ -68,33 +81,40 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
     wl = W.make(name)
     ds = DecodeStep(wl, budget=budget)
     kv = W.kv_bytes(wl)
-    stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    pairs = [(binding.HipEvent(), binding.HipEvent()) for _ in range(steps)]
-    spare = (binding.HipEvent(), binding.HipEvent())
 
-    def one(i):
+    def flush_caches():
         if flush:
             torch.sum(flush_buf, dim=0, out=sink[0])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0, a1 = pairs[i] if i is not None else spare
-        e0.record(stream)
-        ds.step(opts=binding.make_opts(a0, a1))
-        e1.record(stream)
-        return e0, e1
 
     for _ in range(warmup):
-        one(None)
+        flush_caches()
+        ds.step()
     torch.cuda.synchronize()
-    events = []
+
+    # Region 1: whole steps.
+    ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        events.append(one(i))
+    for a, b in ev:
+        flush_caches()
+        a.record()
+        ds.step()
+        b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = np.array([a.elapsed_time(b) for a, b in events])
-    attn_ms = np.array([a.elapsed_ms(b) for a, b in pairs])
+    step_ms = np.array([a.elapsed_ms(b) for a, b in ev])
+
+    # Region 2: the split-attention kernel's own timestamps.
+    kev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in kev:
+        flush_caches()
+        ds.step(opts=binding.make_opts(a, b))
+    torch.cuda.synchronize()
+    attn_ms = np.array([a.elapsed_ms(b) for a, b in kev])
+
     n_tasks = int(ds.n_tasks.item())
     return {
         "workload": name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
@@ -172,15 +192,17 @@ def main():
     head = time_config(args.config, args.steps, args.warmup, flush)
     also = {}
     for name in [x for x in args.also.split(",") if x and x != args.config]:
-        r = time_config(name, max(10, args.steps // 4), max(3, args.warmup // 4), flush)
+        k = max(10, args.steps // 4)
+        r = time_config(name, k, max(3, args.warmup // 4), flush)
         also[name] = {
             "kv_gbs_step": r["kv_bytes"] / r["step_ms_mean"] / 1e6,
             "kv_gbs_attn_kernel": r["kv_bytes"] / r["attn_ms_mean"] / 1e6,
             "frac_hbm_peak_attn": r["kv_bytes"] / r["attn_ms_mean"] / 1e6 / HBM_PEAK_GBS,
-            "steps_per_s": 1e3 / r["step_ms_mean"], "step_ms_mean": r["step_ms_mean"],
-            "attn_ms_mean": r["attn_ms_mean"], "kv_bytes": r["kv_bytes"],
-            "kv_bytes_unique": r["kv_bytes_unique"], "n_tasks": r["n_tasks"], "B": r["B"],
-            "Hq": r["Hq"], "dtype": r["dtype"], "steps": max(10, args.steps // 4),
+            "steps_per_s": 1e3 / r["step_ms_mean"],
+            "step_ms_mean": r["step_ms_mean"], "attn_ms_mean": r["attn_ms_mean"],
+            "kv_bytes": r["kv_bytes"], "kv_bytes_unique": r["kv_bytes_unique"],
+            "n_tasks": r["n_tasks"], "B": r["B"], "Hq": r["Hq"], "Hkv": r["Hkv"],
+            "dtype": r["dtype"], "steps": k,
         }
 
     kv = head["kv_bytes"]
@@ -208,8 +230,9 @@ def main():
         "step_ms_p90": head["step_ms_p90"], "n_tasks": head["n_tasks"], "kv_bytes": kv,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "split_attn_kernel<128,f16,budget>",
-                     "attn_ms_mean": head["attn_ms_mean"]},
+                     "kernel": "kvpage::split_attn_kernel<128, f16, budget, fused queue>",
+                     "attn_ms_mean": head["attn_ms_mean"],
+                     "algorithmic_bytes_per_launch": kv},
         "also": also,
     }
     if not args.no_cpu_baseline:

@@ -198,14 +198,23 @@ def kvpage_debug_gather_offsets(shape, block_tables, tasks, n_tasks, capacity, o
 # Resolved through libkvpage.so's own dependency scope, so they belong to the
 # same HIP runtime instance as the kernels they time.
 
-class HipEvent:
-    """A HIP event (hipEventCreate) for kernel timestamps."""
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
-    def __init__(self):
+
+class HipEvent:
+    """A HIP event for timestamps.  By default created with
+    hipEventDisableSystemFence: timing-only, so recording it does not write
+    back and invalidate caches around the work it brackets."""
+
+    def __init__(self, flags: int = HIP_EVENT_DISABLE_SYSTEM_FENCE):
         h = lib()
         self.handle = ctypes.c_void_p()
-        if h.hipEventCreate(ctypes.byref(self.handle)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if h.hipEventCreateWithFlags(ctypes.byref(self.handle), ctypes.c_uint(flags)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream=None):
+        if lib().hipEventRecord(self.handle, _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def synchronize(self):
         if lib().hipEventSynchronize(self.handle) != 0:
