@@ -181,6 +181,9 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   constexpr int TW = D / 8;    // dwords per lane per tile (K or V)
   constexpr int NPC = E::kPieces;
   constexpr int NT = 2 * kMaxPagesPerTask;
+  // The next task's first tiles are fetched into the slots its first pages
+  // are read from only if the ring length divides the tiles per task.
+  static_assert(NT % DEPTH == 0, "prefetch depth must divide 2 * kMaxPagesPerTask");
   constexpr int QCL = 8 * D / 8 / kWave;          // 16-byte query chunks per lane (8 rows max)
   constexpr int kQStage = 8 * D / 2 + 2 * D;      // staging words: 8 query rows, 2 summary rows
 
