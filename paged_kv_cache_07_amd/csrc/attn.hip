@@ -185,7 +185,11 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   // are read from only if the ring length divides the tiles per task.
   static_assert(NT % DEPTH == 0, "prefetch depth must divide 2 * kMaxPagesPerTask");
   constexpr int QCL = 8 * D / 8 / kWave;          // 16-byte query chunks per lane (8 rows max)
-  constexpr int kQStage = 8 * D / 2 + 2 * D;      // staging words: 8 query rows, 2 summary rows
+  // Staging words per wave: 16 operand rows of D halves (G query heads, then
+  // the summary pieces), then the two float32 summary rows of s_prev.
+  constexpr int kOpRows = 16;
+  constexpr int kQStage = kOpRows * D / 2 + 2 * D;
+  constexpr int DPL = D / kWave;                  // summary elements per lane
 
   // Per-wave LDS: staged query / summary rows, and the scores of the task.
   __shared__ uint32_t lds_q[kWavesPerGroup * kQStage];
@@ -237,7 +241,6 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 
   const int G = p.G;
   const bool is_head = n < G;
-  const bool is_sum = BUDGET && n >= G && n < G + 2 * NPC;
   const bool is_lead = BUDGET && (n == G || n == G + NPC);
 
   // Byte offsets of this lane's pieces inside one (page, head) tile.
@@ -295,21 +298,23 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     u32x4 q[QCL];
     u32x4 s;
   };
+  // Every lane loads (chunks past the group's rows repeat its last chunk), so
+  // that no load is conditional and the wait counts stay exact.
   auto load_rows = [&](const Task& k) {
     Rows w;
     const uint16_t* qblk = p.q + ((int64_t)k.b * p.Hq + (int64_t)k.g * G) * D;
 #pragma unroll
     for (int i = 0; i < QCL; ++i) {
-      const int ch = lane + i * kWave;
-      w.q[i] = ch < G * D / 8 ? *reinterpret_cast<const u32x4*>(qblk + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+      const int ch = min(lane + i * kWave, G * D / 8 - 1);
+      w.q[i] = *reinterpret_cast<const u32x4*>(qblk + 8 * ch);
     }
     w.s = u32x4{0u, 0u, 0u, 0u};
     if constexpr (BUDGET) {
-      const int which = lane / (D / 4);
-      const int ch = lane % (D / 4);
-      if (lane < D / 2)
-        w.s = *reinterpret_cast<const u32x4*>(
-            p.s_prev + (((int64_t)which * p.B + k.b) * p.Hkv + k.g) * D + 4 * ch);
+      const int ls = min(lane, D / 2 - 1);
+      const int which = ls / (D / 4);
+      const int ch = ls % (D / 4);
+      w.s = *reinterpret_cast<const u32x4*>(
+          p.s_prev + (((int64_t)which * p.B + k.b) * p.Hkv + k.g) * D + 4 * ch);
     }
     return w;
   };
@@ -345,61 +350,48 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     }
   };
 
-  uint32_t* qs = lds_q + wave * kQStage;   // [8][D] halves, then [2][D] floats
+  uint32_t* qs = lds_q + wave * kQStage;   // [16][D] halves, then [2][D] floats
   f32x4* S = lds_s[wave][0];               // page i at S[i * kWave + lane]
+  uint16_t* qh = reinterpret_cast<uint16_t*>(qs);
 
-  // Column operand from staged rows: query heads, then summary pieces, zeros.
+  // Column operand from staged rows: query heads, then (budgeting) the
+  // summary pieces, then zeros.  Each summary element is computed once, by
+  // one lane: the group-mean query (heads added in head order), one EMA
+  // step, then pieces in the storage type that sum back to the float32 value.
   auto build_operand = [&](const Rows& rows, u32x4 (&qop)[KB]) {
 #pragma unroll
     for (int i = 0; i < QCL; ++i) *reinterpret_cast<u32x4*>(qs + 4 * (lane + i * kWave)) = rows.q[i];
     if constexpr (BUDGET) {
-      if (lane < D / 2) *reinterpret_cast<u32x4*>(qs + 4 * D + 4 * lane) = rows.s;
+      if (lane < D / 2) *reinterpret_cast<u32x4*>(qs + kOpRows * D / 2 + 4 * lane) = rows.s;
     }
     __builtin_amdgcn_wave_barrier();
+    if constexpr (BUDGET) {
+      const float* sp = reinterpret_cast<const float*>(qs + kOpRows * D / 2);
+#pragma unroll
+      for (int x = 0; x < DPL; ++x) {
+        const int d = DPL * lane + x;
+        float acc = E::value(qh[d]);
+        for (int h = 1; h < G; ++h) acc = __fadd_rn(acc, E::value(qh[h * D + d]));
+        const float qbar = __fmul_rn(acc, p.inv_g);
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+          float rem = ema_step(sp[which * D + d], qbar, which ? p.alpha_slow : p.alpha_fast);
+#pragma unroll
+          for (int piece = 0; piece < NPC; ++piece) {
+            const uint32_t pc = E::bits(rem);
+            qh[(G + which * NPC + piece) * D + d] = (uint16_t)pc;
+            rem = __fsub_rn(rem, E::value(pc));
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    const bool has_row = n < G + (BUDGET ? 2 * NPC : 0);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int d0 = 8 * (4 * kb + r);
-      qop[kb] = is_head ? *reinterpret_cast<const u32x4*>(qs + (n * D + d0) / 2)
+      qop[kb] = has_row ? *reinterpret_cast<const u32x4*>(qs + (n * D + d0) / 2)
                         : u32x4{0u, 0u, 0u, 0u};
-    }
-    if constexpr (BUDGET) {
-      if (is_sum) {
-        // Group-mean query (heads added in head order), one EMA step, then
-        // pieces in the storage type that sum back to the float32 summary.
-        const int which = (n - G) / NPC;
-        const int piece = (n - G) % NPC;
-        const float a = which ? p.alpha_slow : p.alpha_fast;
-        const float* sp = reinterpret_cast<const float*>(qs + 4 * D) + which * D;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int d0 = 8 * (4 * kb + r);
-          float acc[8];
-          for (int h = 0; h < G; ++h) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(qs + (h * D + d0) / 2);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              const float qv = E::value((w[x >> 1] >> (16 * (x & 1))) & 0xffffu);
-              acc[x] = h == 0 ? qv : __fadd_rn(acc[x], qv);
-            }
-          }
-          uint32_t hv[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const float sv = ema_step(sp[d0 + x], __fmul_rn(acc[x], p.inv_g), a);
-            float rem = sv;
-            uint32_t pc = E::bits(rem);
-            for (int k = 0; k < piece; ++k) {
-              rem = __fsub_rn(rem, E::value(pc));
-              pc = E::bits(rem);
-            }
-            hv[x] = pc;
-          }
-          u32x4 v;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) v[x] = hv[2 * x] | (hv[2 * x + 1] << 16);
-          qop[kb] = v;
-        }
-      }
     }
     __builtin_amdgcn_wave_barrier();
   };

@@ -14,6 +14,9 @@
 namespace kvpage {
 
 constexpr int kMergeThreads = 256;
+constexpr int kPagesPerThread = 4;
+constexpr int kPagesPerBlock = kMergeThreads * kPagesPerThread;
+constexpr int kMaxGroup = 8;   // query heads per KV head supported
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -72,130 +75,130 @@ __device__ __forceinline__ int pages_of(int32_t ctx) {
   return ctx > 0 ? (ctx + kPage - 1) / kPage : 0;
 }
 
-// Budgeting finish for query head h of sequence b, given its merged lse
-// (natural log, as stored).  Page p of the sequence lies in split
-// p / pages_per_split of the (b, g) task range starting at `lo`; its raw sum
-// (relative to that task's m) becomes the softmax weight of the page.  The
-// workgroup of the group's first head also writes the page-max tails and the
-// next query-summary state of (b, g).
-template <bool BF>
-__device__ void finish_head(const FinishParams& f, const float* ws_rm, int runlen, int b, int h,
-                            int g, int hh, int B, int Hq, int Hkv, int G, int D, int lo,
-                            float lse_nat) {
-  const int npg = pages_of(f.ctx_lens[b]);
-  const float lse2 = lse_nat * kLog2e;
-  float* mrow = f.page_mass + ((int64_t)b * Hq + h) * f.max_pages;
-  for (int pg = threadIdx.x; pg < f.max_pages; pg += kMergeThreads) {
-    float v = 0.f;
-    if (pg < npg) {
-      const int run = run_of(lo, lo + pg / f.pages_per_split, runlen);
-      v = mrow[pg] * __builtin_amdgcn_exp2f(ws_rm[(int64_t)run * G + hh] - lse2);
-    }
-    mrow[pg] = v;
-  }
-  if (hh != 0) return;
-  for (int k = 0; k < 2; ++k) {
-    float* prow = f.page_max + (((int64_t)k * B + b) * Hkv + g) * f.max_pages;
-    for (int pg = npg + threadIdx.x; pg < f.max_pages; pg += kMergeThreads) prow[pg] = -INFINITY;
-  }
-  const int64_t q0 = ((int64_t)b * Hq + (int64_t)g * G) * D;
-  for (int x = threadIdx.x; x < 2 * D; x += kMergeThreads) {
-    const int which = x >= D;
-    const int d = x - which * D;
-    float acc = q_value<BF>(f.q, q0 + d);
-    for (int hq = 1; hq < G; ++hq) acc = __fadd_rn(acc, q_value<BF>(f.q, q0 + (int64_t)hq * D + d));
-    const int64_t si = (((int64_t)which * B + b) * Hkv + g) * D + d;
-    f.s_next[si] = ema_step(f.s_prev[si], __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
-  }
+// One (sequence, query head) row: its KV head, its head inside the group, and
+// the run partials of the group's task range [lo, lo + n).  All of a
+// workgroup's row metadata is requested at once.
+struct Row {
+  int b, h, g, hh, lo, n, runlen, nrun, npg;
+};
+
+__device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pages) {
+  Row r;
+  r.b = bh / p.Hq;
+  r.h = bh % p.Hq;
+  r.g = r.h / p.G;
+  r.hh = r.h % p.G;
+  const int lo = p.group_offsets[r.b * p.Hkv + r.g];
+  const int hi = p.group_offsets[r.b * p.Hkv + r.g + 1];
+  const int runlen = p.ws_hdr[0];
+  const int ctx = need_pages ? p.fin.ctx_lens[r.b] : 0;
+  r.lo = min(lo, p.capacity);
+  r.n = min(hi, p.capacity) - r.lo;
+  r.runlen = max(1, runlen);
+  r.nrun = run_count(r.lo, r.lo + r.n, r.runlen);
+  r.npg = pages_of(ctx);
+  return r;
 }
 
-// One workgroup per (sequence, query head).  With FINISH the budgeting
-// outputs of that head are finished in the same pass.  Thread (r, c) owns
-// output columns 4c..4c+3 and the splits j = r, r + R, ...; it loads U of
-// them at a time (partial row, m and l together, so one memory latency per
-// batch), keeps its own running max, and the threads are combined at the end
-// with the same log-sum-exp rule in a fixed order.
-template <int D, bool BF, bool FINISH>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p) {
-  constexpr int C4 = D / 4;                // float4 columns of one output row
-  constexpr int R = kMergeThreads / C4;    // partial rows read side by side
-  constexpr int U = 16;                    // splits per thread per batch
-  constexpr int NW = kMergeThreads / kWave;
-  __shared__ float scratch[NW];
-  __shared__ float4 part[R][C4];
-  __shared__ float part_m[R], part_l[R];
+// Index into [capacity][G] arrays of run j of the row, clamped into the
+// arrays so that a load for a missing run (j >= nrun) stays in bounds.
+__device__ __forceinline__ int64_t run_index(const MergeParams& p, const Row& r, int j) {
+  const int jj = min(j, max(r.nrun - 1, 0));
+  const int slot = min(run_slot(r.lo, jj, r.runlen), p.capacity - 1);
+  return (int64_t)slot * p.G + r.hh;
+}
 
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq, h = bh % p.Hq;
-  const int g = h / p.G, hh = h % p.G;
-  const int lo = min(p.group_offsets[b * p.Hkv + g], p.capacity);
-  const int hi = min(p.group_offsets[b * p.Hkv + g + 1], p.capacity);
-  const int n = hi - lo;
-  const int tid = threadIdx.x;
-  uint16_t* orow = p.out + (int64_t)bh * D;
-  if (n <= 0) {
-    for (int d = tid; d < D; d += kMergeThreads) orow[d] = 0;
-    if (tid == 0) p.lse[bh] = -INFINITY;
-    if constexpr (FINISH)
-      finish_head<BF>(p.fin, p.ws_rm, max(1, p.ws_hdr[0]), b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, -INFINITY);
-    return;
+// Log-sum-exp statistics of a row over its run partials: M = max_j m_j and
+// L = sum_j 2^(m_j - M) l_j (log2 domain), in a fixed order, so that every
+// workgroup that needs them gets the same bits.  Returns the natural-log lse
+// exactly as it is stored (-inf for an empty row).
+__device__ float row_lse(const MergeParams& p, const Row& r, float* scratch, float* L_out,
+                         float* M_out) {
+  float tm = -INFINITY, tl = 0.f;
+  for (int j = threadIdx.x; j < max(r.nrun, 1); j += kMergeThreads) {
+    const int64_t i = run_index(p, r, j);
+    const float m = j < r.nrun ? p.ws_rm[i] : -INFINITY;
+    const float l = p.ws_rl[i];
+    const float nm = fmaxf(tm, m);
+    tl = (tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - nm)) +
+         (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - nm));
+    tm = nm;
   }
-  const int c = tid % C4, r = tid / C4;
-  // Run partials of this (b, g): queue positions lo, then multiples of the run length.
-  const int runlen = max(1, p.ws_hdr[0]);
-  const int nrun = run_count(lo, hi, runlen);
+  const float M = block_reduce(tm, true, scratch);
+  const float L = block_reduce(tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - M), false,
+                               scratch);
+  *M_out = M;
+  *L_out = L;
+  return r.n > 0 ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
 
-  float tm = -INFINITY, tl = 0.f;               // this thread's running max / sum
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = r; j0 < nrun; j0 += R * U) {
-    float4 v[U];
-    float mv[U], lv[U];
+// A 32-bit buffer view of `bytes` bytes at `base`: loads past the end read 0
+// and stores past the end are dropped by the hardware, so masked stores need
+// no branch (a masked lane stores to an offset past the end).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+constexpr int kDropOffset = 0x7ffffff0;
+
+__device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rs, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, byte_off, 0, 0);
+}
+
+// Output row of (b, h): out = sum_j 2^(m_j - M) o_j / L over the row's run
+// partials.  Thread (rr, c) owns float4 column c and the runs rr, rr + R, ...,
+// U at a time; the R thread sums are added in LDS in a fixed order.  The first
+// batch is requested before the row statistics; a row with more runs than
+// that batch covers takes the rest in batches of kTailBatch.
+constexpr int kTailBatch = 4;
+
+template <int D, int U>
+struct MergeLoads {
+  static constexpr int C4 = D / 4;
+  static constexpr int R = kMergeThreads / C4;
+  float4 v[U];
+  float m[U];
+
+  __device__ __forceinline__ void issue(const MergeParams& p, const Row& r, int j0) {
+    const int c = threadIdx.x % C4;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * R;
-      if (j < nrun) {
-        const int64_t slot = run_slot(lo, j, runlen);
-        v[u] = *reinterpret_cast<const float4*>(p.ws_o + (slot * p.G + hh) * D + 4 * c);
-        mv[u] = p.ws_rm[slot * p.G + hh];
-        lv[u] = p.ws_rl[slot * p.G + hh];
-      } else {
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        mv[u] = -INFINITY;
-        lv[u] = 0.f;
-      }
+      const int64_t i = run_index(p, r, j);
+      v[u] = *reinterpret_cast<const float4*>(p.ws_o + i * D + 4 * c);
+      m[u] = j < r.nrun ? p.ws_rm[i] : -INFINITY;
     }
-    float bm = mv[0];
-#pragma unroll
-    for (int u = 1; u < U; ++u) bm = fmaxf(bm, mv[u]);
-    const float nm = fmaxf(tm, bm);
-    const float sc = tm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(tm - nm);
-    acc.x *= sc;
-    acc.y *= sc;
-    acc.z *= sc;
-    acc.w *= sc;
-    tl *= sc;
-    tm = nm;
+  }
+
+  __device__ __forceinline__ void add_to(float4& acc, float M) const {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float wu = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u] - nm);
-      acc.x = fmaf(wu, v[u].x, acc.x);
-      acc.y = fmaf(wu, v[u].y, acc.y);
-      acc.z = fmaf(wu, v[u].z, acc.z);
-      acc.w = fmaf(wu, v[u].w, acc.w);
-      tl = fmaf(wu, lv[u], tl);
+      const float w = m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[u] - M);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
     }
   }
-  const float M = block_reduce(tm, true, scratch);
-  const float sc = tm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(tm - M);
-  part[r][c] = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
-  if (c == 0) {
-    part_m[r] = tm;
-    part_l[r] = tl * sc;
+};
+
+template <int D, bool BF, int U>
+__device__ void merge_row(const MergeParams& p, const Row& r, int bh, const MergeLoads<D, U>& first,
+                          float M, float L, float lse_nat) {
+  constexpr int C4 = D / 4;
+  constexpr int R = kMergeThreads / C4;
+  __shared__ float4 part[R][C4];
+  const int tid = threadIdx.x;
+  const int c = tid % C4, rr = tid / C4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  first.add_to(acc, M);
+  for (int j0 = rr + R * U; j0 < r.nrun; j0 += R * kTailBatch) {
+    MergeLoads<D, kTailBatch> more;
+    more.issue(p, r, j0);
+    more.add_to(acc, M);
   }
+  part[rr][c] = acc;
   __syncthreads();
-  float L = 0.f;
-  for (int i = 0; i < R; ++i) L += part_l[i];
-  if (r == 0) {
+  if (rr == 0) {
     float4 t = part[0][c];
     for (int i = 1; i < R; ++i) {
       t.x += part[i][c].x;
@@ -203,26 +206,110 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams 
       t.z += part[i][c].z;
       t.w += part[i][c].w;
     }
-    const float inv = 1.0f / L;
-    const uint32_t w0 = to_bits<BF>(t.x * inv) | ((uint32_t)to_bits<BF>(t.y * inv) << 16);
-    const uint32_t w1 = to_bits<BF>(t.z * inv) | ((uint32_t)to_bits<BF>(t.w * inv) << 16);
-    *reinterpret_cast<uint2*>(orow + 4 * c) = make_uint2(w0, w1);
+    uint32_t w0 = 0, w1 = 0;
+    if (r.n > 0) {
+      const float inv = 1.0f / L;
+      w0 = to_bits<BF>(t.x * inv) | ((uint32_t)to_bits<BF>(t.y * inv) << 16);
+      w1 = to_bits<BF>(t.z * inv) | ((uint32_t)to_bits<BF>(t.w * inv) << 16);
+    }
+    *reinterpret_cast<uint2*>(p.out + (int64_t)bh * D + 4 * c) = make_uint2(w0, w1);
   }
-  const float lse_nat = (M + log2f(L)) * kLn2;
   if (tid == 0) p.lse[bh] = lse_nat;
-  if constexpr (FINISH)
-    finish_head<BF>(p.fin, p.ws_rm, max(1, p.ws_hdr[0]), b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, lse_nat);
 }
 
-// Standalone finish (after a merge already wrote lse): one workgroup per
-// (sequence, query head).
+// Budgeting finish of one slice of kPagesPerBlock logical pages of row (b, h)
+// (GrowPage, Abstract: page-level KV budgeting).  Page pg of the sequence
+// lies in split pg / pages_per_split of the group's task range; the attention
+// kernel left its raw sum relative to the reference max of the run holding
+// that task, so its softmax weight is raw * 2^(m_run - lse / ln 2).  Pages
+// past the sequence get mass 0; for the group's first head the slice also
+// sets the page-max tails to -inf, and slice 0 writes the next query-summary
+// state of (b, g).
+struct PageLoads {
+  float raw[kPagesPerThread], m[kPagesPerThread];
+
+  __device__ __forceinline__ void issue(const MergeParams& p, const Row& r, int bh, int slice) {
+    const FinishParams& f = p.fin;
+    const float* mrow = f.page_mass + (int64_t)bh * f.max_pages;
+    const int last = max(r.npg - 1, 0);
+#pragma unroll
+    for (int k = 0; k < kPagesPerThread; ++k) {
+      const int pg = min(slice * kPagesPerBlock + k * kMergeThreads + (int)threadIdx.x, last);
+      raw[k] = mrow[pg];
+      const int run = run_of(r.lo, r.lo + pg / f.pages_per_split, r.runlen);
+      m[k] = p.ws_rm[(int64_t)min(run, p.capacity - 1) * p.G + r.hh];
+    }
+  }
+};
+
 template <bool BF>
-__global__ void __launch_bounds__(kMergeThreads) finish_kernel(const MergeParams p, int D) {
-  const int bh = blockIdx.x;
-  const int b = bh / p.Hq, h = bh % p.Hq;
-  const int g = h / p.G, hh = h % p.G;
-  const int lo = min(p.group_offsets[b * p.Hkv + g], p.capacity);
-  finish_head<BF>(p.fin, p.ws_rm, max(1, p.ws_hdr[0]), b, h, g, hh, p.B, p.Hq, p.Hkv, p.G, D, lo, p.lse[bh]);
+__device__ void finish_slice(const MergeParams& p, const Row& r, int bh, int slice, int D,
+                             const PageLoads& pl, float lse_nat) {
+  const FinishParams& f = p.fin;
+  const float lse2 = lse_nat * kLog2e;
+  const auto mass = buffer_view(f.page_mass + (int64_t)bh * f.max_pages, f.max_pages * 4);
+#pragma unroll
+  for (int k = 0; k < kPagesPerThread; ++k) {
+    const int pg = slice * kPagesPerBlock + k * kMergeThreads + (int)threadIdx.x;
+    const float v = pg < r.npg ? pl.raw[k] * __builtin_amdgcn_exp2f(pl.m[k] - lse2) : 0.f;
+    buffer_store_f32(v, mass, pg * 4);
+  }
+  if (r.hh != 0) return;
+  for (int which = 0; which < 2; ++which) {
+    const auto pmax = buffer_view(
+        f.page_max + (((int64_t)which * p.B + r.b) * p.Hkv + r.g) * f.max_pages, f.max_pages * 4);
+#pragma unroll
+    for (int k = 0; k < kPagesPerThread; ++k) {
+      const int pg = slice * kPagesPerBlock + k * kMergeThreads + (int)threadIdx.x;
+      buffer_store_f32(-INFINITY, pmax, pg >= r.npg ? pg * 4 : kDropOffset);
+    }
+  }
+  if (slice != 0 || (int)threadIdx.x >= 2 * D) return;
+  // Next summary state: group-mean query, heads added in head order.
+  const int which = (int)threadIdx.x >= D;
+  const int d = threadIdx.x - which * D;
+  const int64_t q0 = ((int64_t)r.b * p.Hq + (int64_t)r.g * p.G) * D + d;
+  float qv[kMaxGroup];
+#pragma unroll
+  for (int hq = 0; hq < kMaxGroup; ++hq) qv[hq] = q_value<BF>(f.q, q0 + (int64_t)min(hq, p.G - 1) * D);
+  const int64_t si = (((int64_t)which * p.B + r.b) * p.Hkv + r.g) * D + d;
+  const float sp = f.s_prev[si];
+  float acc = qv[0];
+#pragma unroll
+  for (int hq = 1; hq < kMaxGroup; ++hq)
+    if (hq < p.G) acc = __fadd_rn(acc, qv[hq]);
+  f.s_next[si] = ema_step(sp, __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
+}
+
+// One workgroup per (row, page slice): slice 0 merges the output row, and
+// with FINISH every slice finishes its pages of the budgeting outputs.  All
+// of a workgroup's loads are requested before the row statistics are
+// reduced, so the data arrives in one memory round trip.
+template <int D, bool BF, bool FINISH, int U>
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p, int nslice) {
+  __shared__ float scratch[kMergeThreads / kWave];
+  const int bh = blockIdx.x / nslice, slice = blockIdx.x % nslice;
+  const Row r = row_of(p, bh, FINISH);
+  MergeLoads<D, U> ml;
+  PageLoads pl;
+  const int rr = threadIdx.x / MergeLoads<D, U>::C4;
+  if (slice == 0) ml.issue(p, r, rr);
+  if constexpr (FINISH) pl.issue(p, r, bh, slice);
+  float M, L;
+  const float lse_nat = row_lse(p, r, scratch, &L, &M);
+  if (slice == 0) merge_row<D, BF, U>(p, r, bh, ml, M, L, lse_nat);
+  if constexpr (FINISH) finish_slice<BF>(p, r, bh, slice, D, pl, lse_nat);
+}
+
+// Standalone finish after a merge that already wrote lse: one workgroup per
+// slice of pages of one row.
+template <bool BF>
+__global__ void __launch_bounds__(kMergeThreads) finish_kernel(const MergeParams p, int D, int nslice) {
+  const int bh = blockIdx.x / nslice, slice = blockIdx.x % nslice;
+  const Row r = row_of(p, bh, true);
+  PageLoads pl;
+  pl.issue(p, r, bh, slice);
+  finish_slice<BF>(p, r, bh, slice, D, pl, p.lse[bh]);
 }
 
 static MergeParams merge_params(const kvpage_shape& s, const int32_t* group_offsets,
@@ -257,16 +344,34 @@ static MergeParams merge_params(const kvpage_shape& s, const int32_t* group_offs
   return p;
 }
 
+static int page_slices(const kvpage_shape& s) {
+  return (s.max_pages + kPagesPerBlock - 1) / kPagesPerBlock;
+}
+
+// A small grid is bound by one workgroup's memory latency: its threads take
+// 16 runs each in the first batch.  A large grid is bound by how many
+// workgroups are resident: 4 runs each keep the register count low.
+constexpr int kSmallMergeGrid = 1024;
+
+template <int D, bool BF, bool FINISH>
+static void launch_merge_d(int grid, const MergeParams& p, int nslice, hipStream_t stream) {
+  if (grid <= kSmallMergeGrid)
+    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 16>), dim3(grid), dim3(kMergeThreads), 0, stream, p, nslice);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 4>), dim3(grid), dim3(kMergeThreads), 0, stream, p, nslice);
+}
+
 template <bool FINISH>
 static void launch_merge_variant(const kvpage_shape& s, const MergeParams& p, hipStream_t stream) {
-  const int grid = s.B * s.Hq;
+  const int nslice = FINISH ? page_slices(s) : 1;
+  const int grid = s.B * s.Hq * nslice;
   const bool bf = s.dtype == KVPAGE_BF16;
   if (s.d == 128) {
-    if (bf) hipLaunchKernelGGL((merge_kernel<128, true, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
-    else hipLaunchKernelGGL((merge_kernel<128, false, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
+    if (bf) launch_merge_d<128, true, FINISH>(grid, p, nslice, stream);
+    else launch_merge_d<128, false, FINISH>(grid, p, nslice, stream);
   } else {
-    if (bf) hipLaunchKernelGGL((merge_kernel<64, true, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
-    else hipLaunchKernelGGL((merge_kernel<64, false, FINISH>), dim3(grid), dim3(kMergeThreads), 0, stream, p);
+    if (bf) launch_merge_d<64, true, FINISH>(grid, p, nslice, stream);
+    else launch_merge_d<64, false, FINISH>(grid, p, nslice, stream);
   }
 }
 
@@ -297,11 +402,12 @@ hipError_t launch_page_mass(const kvpage_shape& s, const kvpage_budget& bud, con
   if (s.B * s.Hq <= 0) return hipSuccess;
   const MergeParams p = merge_params(s, group_offsets, capacity, workspace, nullptr,
                                      const_cast<float*>(lse), &bud, q, ctx_lens);
-  const int grid = s.B * s.Hq;
+  const int nslice = page_slices(s);
+  const int grid = s.B * s.Hq * nslice;
   if (s.dtype == KVPAGE_BF16)
-    hipLaunchKernelGGL(finish_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d);
+    hipLaunchKernelGGL(finish_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d, nslice);
   else
-    hipLaunchKernelGGL(finish_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d);
+    hipLaunchKernelGGL(finish_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d, nslice);
   return hipGetLastError();
 }
 
