@@ -145,33 +145,33 @@ __device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t
 }
 
 // Output row of (b, h): out = sum_j 2^(m_j - M) o_j / L over the row's run
-// partials.  Thread (rr, c) owns float4 column c and the runs rr, rr + R, ...,
-// U at a time; the R thread sums are added in LDS in a fixed order.  The first
-// batch is requested before the row statistics; a row with more runs than
-// that batch covers takes the rest in batches of kTailBatch.
-constexpr int kTailBatch = 4;
+// partials.  The D columns are split into CG groups, one per workgroup of the
+// row.  Thread (rr, c) owns float4 column c of its group and the runs rr,
+// rr + R, ..., kMergeBatch at a time; the R thread sums are added in LDS in a
+// fixed order.  The first batch is requested before the row statistics.
+constexpr int kMergeBatch = 4;
 
-template <int D, int U>
+template <int D, int CG>
 struct MergeLoads {
-  static constexpr int C4 = D / 4;
+  static constexpr int C4 = D / 4 / CG;   // float4 columns per workgroup
   static constexpr int R = kMergeThreads / C4;
-  float4 v[U];
-  float m[U];
+  float4 v[kMergeBatch];
+  float m[kMergeBatch];
 
-  __device__ __forceinline__ void issue(const MergeParams& p, const Row& r, int j0) {
+  __device__ __forceinline__ void issue(const MergeParams& p, const Row& r, int j0, int col0) {
     const int c = threadIdx.x % C4;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const int j = j0 + u * R;
       const int64_t i = run_index(p, r, j);
-      v[u] = *reinterpret_cast<const float4*>(p.ws_o + i * D + 4 * c);
+      v[u] = *reinterpret_cast<const float4*>(p.ws_o + i * D + col0 + 4 * c);
       m[u] = j < r.nrun ? p.ws_rm[i] : -INFINITY;
     }
   }
 
   __device__ __forceinline__ void add_to(float4& acc, float M) const {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kMergeBatch; ++u) {
       const float w = m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[u] - M);
       acc.x = fmaf(w, v[u].x, acc.x);
       acc.y = fmaf(w, v[u].y, acc.y);
@@ -181,26 +181,25 @@ struct MergeLoads {
   }
 };
 
-template <int D, bool BF, int U>
-__device__ void merge_row(const MergeParams& p, const Row& r, int bh, const MergeLoads<D, U>& first,
-                          float M, float L, float lse_nat) {
-  constexpr int C4 = D / 4;
-  constexpr int R = kMergeThreads / C4;
-  __shared__ float4 part[R][C4];
+template <int D, bool BF, int CG>
+__device__ void merge_cols(const MergeParams& p, const Row& r, int bh, int col0,
+                           const MergeLoads<D, CG>& first, float M, float L) {
+  using ML = MergeLoads<D, CG>;
+  __shared__ float4 part[ML::R][ML::C4];
   const int tid = threadIdx.x;
-  const int c = tid % C4, rr = tid / C4;
+  const int c = tid % ML::C4, rr = tid / ML::C4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   first.add_to(acc, M);
-  for (int j0 = rr + R * U; j0 < r.nrun; j0 += R * kTailBatch) {
-    MergeLoads<D, kTailBatch> more;
-    more.issue(p, r, j0);
+  for (int j0 = rr + ML::R * kMergeBatch; j0 < r.nrun; j0 += ML::R * kMergeBatch) {
+    ML more;
+    more.issue(p, r, j0, col0);
     more.add_to(acc, M);
   }
   part[rr][c] = acc;
   __syncthreads();
   if (rr == 0) {
     float4 t = part[0][c];
-    for (int i = 1; i < R; ++i) {
+    for (int i = 1; i < ML::R; ++i) {
       t.x += part[i][c].x;
       t.y += part[i][c].y;
       t.z += part[i][c].z;
@@ -212,9 +211,8 @@ __device__ void merge_row(const MergeParams& p, const Row& r, int bh, const Merg
       w0 = to_bits<BF>(t.x * inv) | ((uint32_t)to_bits<BF>(t.y * inv) << 16);
       w1 = to_bits<BF>(t.z * inv) | ((uint32_t)to_bits<BF>(t.w * inv) << 16);
     }
-    *reinterpret_cast<uint2*>(p.out + (int64_t)bh * D + 4 * c) = make_uint2(w0, w1);
+    *reinterpret_cast<uint2*>(p.out + (int64_t)bh * D + col0 + 4 * c) = make_uint2(w0, w1);
   }
-  if (tid == 0) p.lse[bh] = lse_nat;
 }
 
 // Budgeting finish of one slice of kPagesPerBlock logical pages of row (b, h)
@@ -281,24 +279,28 @@ __device__ void finish_slice(const MergeParams& p, const Row& r, int bh, int sli
   f.s_next[si] = ema_step(sp, __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
 }
 
-// One workgroup per (row, page slice): slice 0 merges the output row, and
-// with FINISH every slice finishes its pages of the budgeting outputs.  All
-// of a workgroup's loads are requested before the row statistics are
-// reduced, so the data arrives in one memory round trip.
-template <int D, bool BF, bool FINISH, int U>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p, int nslice) {
+// Each row has nsub = max(CG, nslice) workgroups: workgroup k merges column
+// group k (k < CG) and, with FINISH, finishes page slice k (k < nslice).
+// All of a workgroup's loads are requested before the row statistics are
+// reduced, so its data arrives in one memory round trip.
+template <int D, bool BF, bool FINISH, int CG>
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p, int nslice,
+                                                              int nsub) {
   __shared__ float scratch[kMergeThreads / kWave];
-  const int bh = blockIdx.x / nslice, slice = blockIdx.x % nslice;
+  const int bh = blockIdx.x / nsub, sub = blockIdx.x % nsub;
   const Row r = row_of(p, bh, FINISH);
-  MergeLoads<D, U> ml;
+  const bool do_cols = sub < CG;
+  const bool do_pages = FINISH && sub < nslice;
+  const int col0 = sub * (D / CG);
+  MergeLoads<D, CG> ml;
   PageLoads pl;
-  const int rr = threadIdx.x / MergeLoads<D, U>::C4;
-  if (slice == 0) ml.issue(p, r, rr);
-  if constexpr (FINISH) pl.issue(p, r, bh, slice);
+  if (do_cols) ml.issue(p, r, threadIdx.x / MergeLoads<D, CG>::C4, col0);
+  if (do_pages) pl.issue(p, r, bh, sub);
   float M, L;
   const float lse_nat = row_lse(p, r, scratch, &L, &M);
-  if (slice == 0) merge_row<D, BF, U>(p, r, bh, ml, M, L, lse_nat);
-  if constexpr (FINISH) finish_slice<BF>(p, r, bh, slice, D, pl, lse_nat);
+  if (do_cols) merge_cols<D, BF, CG>(p, r, bh, col0, ml, M, L);
+  if (sub == 0 && threadIdx.x == 0) p.lse[bh] = lse_nat;
+  if (do_pages) finish_slice<BF>(p, r, bh, sub, D, pl, lse_nat);
 }
 
 // Standalone finish after a merge that already wrote lse: one workgroup per
@@ -348,30 +350,35 @@ static int page_slices(const kvpage_shape& s) {
   return (s.max_pages + kPagesPerBlock - 1) / kPagesPerBlock;
 }
 
-// A small grid is bound by one workgroup's memory latency: its threads take
-// 16 runs each in the first batch.  A large grid is bound by how many
-// workgroups are resident: 4 runs each keep the register count low.
-constexpr int kSmallMergeGrid = 1024;
+// Few rows: each row's output is merged by 4 workgroups (a quarter of the
+// columns each), so the partials are read by 4x as many compute units.  Many
+// rows: one workgroup merges a whole row.
+constexpr int kSplitColumnsMaxRows = 1024;
 
 template <int D, bool BF, bool FINISH>
-static void launch_merge_d(int grid, const MergeParams& p, int nslice, hipStream_t stream) {
-  if (grid <= kSmallMergeGrid)
-    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 16>), dim3(grid), dim3(kMergeThreads), 0, stream, p, nslice);
-  else
-    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 4>), dim3(grid), dim3(kMergeThreads), 0, stream, p, nslice);
+static void launch_merge_d(int rows, int nslice, const MergeParams& p, hipStream_t stream) {
+  if (rows <= kSplitColumnsMaxRows) {
+    const int nsub = nslice > 4 ? nslice : 4;
+    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 4>), dim3(rows * nsub), dim3(kMergeThreads), 0,
+                       stream, p, nslice, nsub);
+  } else {
+    const int nsub = nslice;
+    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 1>), dim3(rows * nsub), dim3(kMergeThreads), 0,
+                       stream, p, nslice, nsub);
+  }
 }
 
 template <bool FINISH>
 static void launch_merge_variant(const kvpage_shape& s, const MergeParams& p, hipStream_t stream) {
+  const int rows = s.B * s.Hq;
   const int nslice = FINISH ? page_slices(s) : 1;
-  const int grid = s.B * s.Hq * nslice;
   const bool bf = s.dtype == KVPAGE_BF16;
   if (s.d == 128) {
-    if (bf) launch_merge_d<128, true, FINISH>(grid, p, nslice, stream);
-    else launch_merge_d<128, false, FINISH>(grid, p, nslice, stream);
+    if (bf) launch_merge_d<128, true, FINISH>(rows, nslice, p, stream);
+    else launch_merge_d<128, false, FINISH>(rows, nslice, p, stream);
   } else {
-    if (bf) launch_merge_d<64, true, FINISH>(grid, p, nslice, stream);
-    else launch_merge_d<64, false, FINISH>(grid, p, nslice, stream);
+    if (bf) launch_merge_d<64, true, FINISH>(rows, nslice, p, stream);
+    else launch_merge_d<64, false, FINISH>(rows, nslice, p, stream);
   }
 }
 
