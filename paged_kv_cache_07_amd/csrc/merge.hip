@@ -303,6 +303,142 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams 
   if (do_pages) finish_slice<BF>(p, r, bh, sub, D, pl, lse_nat);
 }
 
+// ---- Many rows: one wavefront per (row, page slice) ----------------------
+//
+// With hundreds of rows each has few runs, and the cost is the chain of
+// dependent round trips per workgroup and how many are resident.  Here a
+// wavefront owns one (row, slice of kPagesPerBlock pages): it requests the
+// row's run statistics, (slice 0) the run partials of its 64 x D/64 output
+// columns, and its slice's raw page sums and run maxima at once, then reduces
+// with cross-lane shuffles only (no LDS, no barrier).  The butterfly gives
+// every lane, and every wavefront of the row, the same bits.
+constexpr int kWavePagesPerLane = kPagesPerBlock / kWave;   // 16
+constexpr int kWaveRunBatch = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <int D, bool BF, bool FINISH>
+__global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergeParams p, int nslice) {
+  constexpr int CPL = D / kWave;   // output columns per lane (1 or 2)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = blockIdx.x * (kMergeThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= p.B * p.Hq * nslice) return;
+  const int bh = item / nslice, slice = item % nslice;
+  const Row r = row_of(p, bh, FINISH);
+  const bool do_out = slice == 0;
+
+  // Run partials of this lane's columns, first batch.
+  float ov[kWaveRunBatch][CPL], om[kWaveRunBatch];
+  auto issue_runs = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < kWaveRunBatch; ++u) {
+      const int64_t i = run_index(p, r, j0 + u);
+      const float* src = p.ws_o + i * D + CPL * lane;
+#pragma unroll
+      for (int x = 0; x < CPL; ++x) ov[u][x] = src[x];
+      om[u] = j0 + u < r.nrun ? p.ws_rm[i] : -INFINITY;
+    }
+  };
+  if (do_out) issue_runs(0);
+  // Raw page sums of the slice and the run maxima they are relative to.
+  float raw[kWavePagesPerLane], rmx[kWavePagesPerLane];
+  if constexpr (FINISH) {
+    const FinishParams& f = p.fin;
+    const float* mrow = f.page_mass + (int64_t)bh * f.max_pages;
+    const int last = max(r.npg - 1, 0);
+#pragma unroll
+    for (int k = 0; k < kWavePagesPerLane; ++k) {
+      const int pg = min(slice * kPagesPerBlock + k * kWave + lane, last);
+      raw[k] = mrow[pg];
+      const int run = run_of(r.lo, r.lo + pg / f.pages_per_split, r.runlen);
+      rmx[k] = p.ws_rm[(int64_t)min(run, p.capacity - 1) * p.G + r.hh];
+    }
+  }
+  // Row statistics over all runs, lanes strided over the runs.
+  float tm = -INFINITY, tl = 0.f;
+  for (int j = lane; j < max(r.nrun, 1); j += kWave) {
+    const int64_t i = run_index(p, r, j);
+    const float m = j < r.nrun ? p.ws_rm[i] : -INFINITY;
+    const float l = p.ws_rl[i];
+    const float nm = fmaxf(tm, m);
+    tl = (tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - nm)) +
+         (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - nm));
+    tm = nm;
+  }
+  const float M = wave_max(tm);
+  const float L = wave_sum(tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - M));
+  const float lse_nat = r.n > 0 ? (M + log2f(L)) * kLn2 : -INFINITY;
+
+  if (do_out) {
+    float acc[CPL];
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) acc[x] = 0.f;
+    for (int j0 = 0;;) {
+#pragma unroll
+      for (int u = 0; u < kWaveRunBatch; ++u) {
+        const float w = om[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om[u] - M);
+#pragma unroll
+        for (int x = 0; x < CPL; ++x) acc[x] = fmaf(w, ov[u][x], acc[x]);
+      }
+      j0 += kWaveRunBatch;
+      if (j0 >= r.nrun) break;
+      issue_runs(j0);
+    }
+    const float inv = r.n > 0 ? 1.0f / L : 0.f;
+    uint16_t* orow = p.out + (int64_t)bh * D + CPL * lane;
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) orow[x] = r.n > 0 ? to_bits<BF>(acc[x] * inv) : (uint16_t)0;
+    if (lane == 0) p.lse[bh] = lse_nat;
+  }
+  if constexpr (FINISH) {
+    const FinishParams& f = p.fin;
+    const float lse2 = lse_nat * kLog2e;
+    const auto mass = buffer_view(f.page_mass + (int64_t)bh * f.max_pages, f.max_pages * 4);
+#pragma unroll
+    for (int k = 0; k < kWavePagesPerLane; ++k) {
+      const int pg = slice * kPagesPerBlock + k * kWave + lane;
+      const float v = pg < r.npg ? raw[k] * __builtin_amdgcn_exp2f(rmx[k] - lse2) : 0.f;
+      buffer_store_f32(v, mass, pg * 4);
+    }
+    if (r.hh != 0) return;
+    for (int which = 0; which < 2; ++which) {
+      const auto pmax = buffer_view(
+          f.page_max + (((int64_t)which * p.B + r.b) * p.Hkv + r.g) * f.max_pages, f.max_pages * 4);
+#pragma unroll
+      for (int k = 0; k < kWavePagesPerLane; ++k) {
+        const int pg = slice * kPagesPerBlock + k * kWave + lane;
+        buffer_store_f32(-INFINITY, pmax, pg >= r.npg ? pg * 4 : kDropOffset);
+      }
+    }
+    if (slice != 0) return;
+    // Next summary state of (b, g): 2*D elements over the 64 lanes.
+#pragma unroll
+    for (int e = 0; e < 2 * CPL; ++e) {
+      const int x = e * kWave + lane;
+      const int which = x >= D;
+      const int d = x - which * D;
+      const int64_t q0 = ((int64_t)r.b * p.Hq + (int64_t)r.g * p.G) * D + d;
+      float qv[kMaxGroup];
+#pragma unroll
+      for (int hq = 0; hq < kMaxGroup; ++hq) qv[hq] = q_value<BF>(f.q, q0 + (int64_t)min(hq, p.G - 1) * D);
+      const int64_t si = (((int64_t)which * p.B + r.b) * p.Hkv + r.g) * D + d;
+      const float sp = f.s_prev[si];
+      float acc = qv[0];
+#pragma unroll
+      for (int hq = 1; hq < kMaxGroup; ++hq)
+        if (hq < p.G) acc = __fadd_rn(acc, qv[hq]);
+      f.s_next[si] = ema_step(sp, __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
+    }
+  }
+}
+
 // Standalone finish after a merge that already wrote lse: one workgroup per
 // slice of pages of one row.
 template <bool BF>
@@ -352,19 +488,20 @@ static int page_slices(const kvpage_shape& s) {
 
 // Few rows: each row's output is merged by 4 workgroups (a quarter of the
 // columns each), so the partials are read by 4x as many compute units.  Many
-// rows: one workgroup merges a whole row.
-constexpr int kSplitColumnsMaxRows = 1024;
+// rows: one wavefront per (row, page slice).
+constexpr int kWaveMergeMinRows = 512;
 
 template <int D, bool BF, bool FINISH>
 static void launch_merge_d(int rows, int nslice, const MergeParams& p, hipStream_t stream) {
-  if (rows <= kSplitColumnsMaxRows) {
+  if (rows < kWaveMergeMinRows) {
     const int nsub = nslice > 4 ? nslice : 4;
     hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 4>), dim3(rows * nsub), dim3(kMergeThreads), 0,
                        stream, p, nslice, nsub);
   } else {
-    const int nsub = nslice;
-    hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 1>), dim3(rows * nsub), dim3(kMergeThreads), 0,
-                       stream, p, nslice, nsub);
+    const int waves_per_block = kMergeThreads / kWave;
+    const int grid = (rows * nslice + waves_per_block - 1) / waves_per_block;
+    hipLaunchKernelGGL((merge_wave_kernel<D, BF, FINISH>), dim3(grid), dim3(kMergeThreads), 0,
+                       stream, p, nslice);
   }
 }
 

@@ -214,7 +214,7 @@ def make(name: str, seed: int | None = None, ctx_divisor: int = 1, threads=None,
     with the same head shape, dtype, page structure and length mix).
     """
     base = {"tiny": 1000, "b1": 1001, "b8_bimodal": 1002, "b8_uniform": 1102,
-            "b8_zipf": 1003, "b64_prefix": 1004}
+            "b8_zipf": 1003, "b64_prefix": 1004, "b4_bimodal": 1005}
     if name not in base:
         raise KeyError(name)
     seed = base[name] if seed is None else seed
@@ -229,9 +229,12 @@ def make(name: str, seed: int | None = None, ctx_divisor: int = 1, threads=None,
         ctx = _ctx_scale([32768], ctx_divisor, 16)
         return _assemble(name, seed, rng, ctx, 32, 8, 128, 16, split_tokens, F16,
                          max(4096 // ctx_divisor, -(-ctx[0] // 16) + 1), **kw)
-    if name in ("b8_bimodal", "b8_uniform"):
+    if name in ("b8_bimodal", "b8_uniform", "b4_bimodal"):
         if name == "b8_bimodal":
             ctx = np.concatenate([rng.integers(512, 2048 + 1, 4), rng.integers(24576, 65536 + 1, 4)])
+        elif name == "b4_bimodal":
+            # The B4 bimodal mix: 2 short and 2 long sequences.
+            ctx = np.concatenate([rng.integers(512, 2048 + 1, 2), rng.integers(24576, 65536 + 1, 2)])
         else:
             ctx = rng.integers(512, 65536 + 1, 8)
         ctx = _ctx_scale(ctx, ctx_divisor, 16)
@@ -259,7 +262,7 @@ def make(name: str, seed: int | None = None, ctx_divisor: int = 1, threads=None,
                      shared_prefix_pages=shared, **kw)
 
 
-NAMES = ("tiny", "b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix")
+NAMES = ("tiny", "b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix", "b4_bimodal")
 
 
 def custom(ctx, Hq, Hkv, d, page_size=16, split_tokens=256, dtype=F16, seed=7,

@@ -136,14 +136,15 @@ def test_tiny_all_outputs(split):
 
 
 @pytest.mark.parametrize("name,div", [("b1", 16), ("b8_bimodal", 32), ("b8_uniform", 32),
-                                      ("b8_zipf", 64), ("b64_prefix", 16)])
+                                      ("b8_zipf", 64), ("b64_prefix", 16), ("b4_bimodal", 32)])
 def test_oracle_sized_configs_all_outputs(name, div):
     wl = W.make(name, ctx_divisor=div)
     _, res = _run(wl, label=f"{name}/{div}")
     compare_step(res, oracle_step(wl), label=name)
 
 
-@pytest.mark.parametrize("name", ["b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix"])
+@pytest.mark.parametrize("name", ["b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix",
+                                  "b4_bimodal"])
 def test_full_size_sampled_rows(name):
     wl = W.make(name)
     _, res = _run(wl, label=f"{name}-full")
