@@ -409,6 +409,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   int run_start = t_first;
   int run_lp0 = cur.lp0;
   int run_pages = 0;
+  // A run is consecutive tasks of one (sequence, KV head); all but its last
+  // are whole splits of pps pages, so page pp of the run is page pp % pps of
+  // its task pp / pps.
+  const int pps = p.split_tokens / kPage;
   float mrun = is_head ? -INFINITY : INFINITY;   // log2-domain reference; non-head lanes weigh 0
   float l = 0.f;
   f32x4 O[VD];
@@ -590,15 +594,17 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), h));
           float* row = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0;
           for (int pp = lane; pp < run_pages; pp += kWave) {
-            const int kk = pp >> 4;
-            row[pp] = lds_mass[wave][kk][h][pp & 15] *
+            const int kk = pp / pps;   // task of the run holding page pp
+            row[pp] = lds_mass[wave][kk][h][pp - kk * pps] *
                       __builtin_amdgcn_exp2f(lds_tref[wave][kk][h] - mh);
           }
         }
         for (int which = 0; which < 2; ++which) {
           float* row = p.page_max + (((int64_t)which * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0;
-          for (int pp = lane; pp < run_pages; pp += kWave)
-            row[pp] = lds_pmax[wave][pp >> 4][which][pp & 15];
+          for (int pp = lane; pp < run_pages; pp += kWave) {
+            const int kk = pp / pps;
+            row[pp] = lds_pmax[wave][kk][which][pp - kk * pps];
+          }
         }
       }
       if (!has_next) break;

@@ -286,11 +286,13 @@ def test_one_call_step_equals_separate_calls(budget):
             compare_step(rb, oracle_step(wl), label=name)
 
 
-@pytest.mark.parametrize("max_wg", [1, 3])
-def test_long_wave_runs_fold_consecutive_tasks(max_wg):
+@pytest.mark.parametrize("max_wg,split", [(1, 256), (3, 256), (1, 64), (3, 32), (2, 128)])
+def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
     """Few workgroups: each wavefront walks a long stretch of the queue,
     folding consecutive tasks of one (sequence, KV head) into one partial and
-    crossing group boundaries inside its stretch."""
+    crossing group boundaries inside its stretch.  Splits shorter than 16
+    pages put several short tasks in one run, whose staged page values must
+    land on the right logical pages."""
     from paged_kv_cache_07_amd import binding
     from paged_kv_cache_07_amd.device import DecodeStep
     cases = [W.make("b8_bimodal", ctx_divisor=32), W.make("b64_prefix", ctx_divisor=16),
@@ -299,8 +301,9 @@ def test_long_wave_runs_fold_consecutive_tasks(max_wg):
     for wl in cases:
         wl.s_prev = np.random.default_rng(8).standard_normal(wl.s_prev.shape).astype(np.float32)
         for budget in (True, False):
-            say("long-runs", wl.name, "max_wg", max_wg, "budget", budget)
-            ds = DecodeStep(wl, budget=budget)
+            say("long-runs", wl.name, "max_wg", max_wg, "split", split, "budget", budget)
+            ds = DecodeStep(wl, budget=budget, split_tokens=split)
             ds.step(opts=binding.make_opts(max_workgroups=max_wg))
             res = ds.results()
-            compare_step(res, oracle_step(wl), budget=budget, label=f"{wl.name} wg{max_wg}")
+            compare_step(res, oracle_step(wl, split_tokens=split), budget=budget,
+                         label=f"{wl.name} wg{max_wg} S{split}")
