@@ -107,7 +107,7 @@ struct AttnParams {
 };
 
 constexpr int kWavesPerGroup = 4;
-constexpr int kMaxPagesPerTask = 16;
+constexpr int kMaxPagesPerTask = 16;   // pages of the longest split (256 tokens)
 constexpr int kRunMax = 16;   // most queue positions one wavefront takes in a row
 
 // All-reduce over the four 16-lane rows of a wavefront (lanes n, n+16, n+32,
@@ -171,7 +171,7 @@ __device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, 
   return q;
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const AttnParams p) {
   using E = Elem<BF>;
@@ -180,10 +180,16 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   constexpr int VW = VD / 2;   // V dwords per lane per token
   constexpr int TW = D / 8;    // dwords per lane per tile (K or V)
   constexpr int NPC = E::kPieces;
-  constexpr int NT = 2 * kMaxPagesPerTask;
+  // PPT: pages per task this instance handles (the split is at most PPT
+  // pages); every task issues loads for exactly PPT K and PPT V tiles.
+  static_assert(PPT <= kMaxPagesPerTask, "at most 16 pages per task");
+  constexpr int NT = 2 * PPT;
   // The next task's first tiles are fetched into the slots its first pages
   // are read from only if the ring length divides the tiles per task.
-  static_assert(NT % DEPTH == 0, "prefetch depth must divide 2 * kMaxPagesPerTask");
+  static_assert(NT % DEPTH == 0, "prefetch depth must divide the tiles per task");
+  // The next task is known only after this task's K pass, so the tiles the
+  // ring fetches ahead of it during the V pass must all be K tiles.
+  static_assert(DEPTH <= PPT, "prefetch depth must not exceed the K tiles of a task");
   constexpr int QCL = 8 * D / 8 / kWave;          // 16-byte query chunks per lane (8 rows max)
   // Staging words per wave: 16 operand rows of D halves (G query heads, then
   // the summary pieces), then the two float32 summary rows of s_prev.
@@ -193,7 +199,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 
   // Per-wave LDS: staged query / summary rows, and the scores of the task.
   __shared__ uint32_t lds_q[kWavesPerGroup * kQStage];
-  __shared__ f32x4 lds_s[kWavesPerGroup][kMaxPagesPerTask][kWave];
+  __shared__ f32x4 lds_s[kWavesPerGroup][PPT][kWave];
   // Per-wave staging of a run's per-task outputs, written out once per run:
   // raw page sums per head, summary page maxima, the weight reference each
   // task used, and (fused queue build) the task records.
@@ -321,8 +327,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   // Tile tau of a task: K page tau for tau < 16, V page tau - 16 after.  Pages
   // past npg - 1 repeat the last page (the load count never depends on npg).
   auto load_tile = [&](const Task& k, int32_t ids, int tau, uint32_t (&dst)[TW]) {
-    const bool is_v = tau >= kMaxPagesPerTask;
-    const int pg = min(is_v ? tau - kMaxPagesPerTask : tau, k.npg - 1);
+    const bool is_v = tau >= PPT;
+    const int pg = min(is_v ? tau - PPT : tau, k.npg - 1);
     const int32_t pid = __builtin_amdgcn_readlane(ids, pg);
     const int64_t off = tile_offset(pid, k.g, p.Hkv, D) * 2;
     if (!is_v) {
@@ -426,7 +432,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     float keep[4] = {0.f, 0.f, 0.f, 0.f};  // per-page outputs, page 4*r + u
     float mloc = -INFINITY;                 // in-lane max of this lane's scores
 #pragma unroll
-    for (int i = 0; i < kMaxPagesPerTask; ++i) {
+    for (int i = 0; i < PPT; ++i) {
       const int slot = i % DEPTH;
       if (i < npg) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -491,8 +497,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 
     // ---- pass 2: weights, page sums, P V into the run's accumulators ----
 #pragma unroll
-    for (int i = 0; i < kMaxPagesPerTask; ++i) {
-      const int tau = kMaxPagesPerTask + i;
+    for (int i = 0; i < PPT; ++i) {
+      const int tau = PPT + i;
       const int slot = tau % DEPTH;
       if (i < npg) {
         const f32x4 sc = S[i * kWave + lane];
@@ -626,10 +632,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   }
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT>
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
-  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ>;
+  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT>;
   static int blocks_per_cu[64] = {0};
   static int num_cus[64] = {0};
   int dev = 0;
@@ -662,27 +668,43 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
   return hipGetLastError();
 }
 
-// Tiles (4 KiB at d = 128) each wave keeps in flight.
+// Tiles (4 KiB at d = 128) each wave keeps in flight.  Two is fastest on
+// MI355X for every workload measured: with 1024 wavefronts, 8 tiles each put
+// 32 MiB in flight, as much as all XCDs' L2 together, and ran 3-8% slower;
+// one tile each cannot cover the memory latency.
 #ifndef KVPAGE_ATTN_DEPTH
-#define KVPAGE_ATTN_DEPTH 8
+#define KVPAGE_ATTN_DEPTH 2
 #endif
 
+template <bool FUSEDQ, int PPT>
+static hipError_t dispatch_ppt(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
+                               hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                               int max_wg) {
+  constexpr int DP = KVPAGE_ATTN_DEPTH < PPT ? KVPAGE_ATTN_DEPTH : PPT;
+  const bool bf = s.dtype == KVPAGE_BF16;
+  if (s.d == 128) {
+    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                       : launch_one<128, true, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
+               : launch_one<128, false, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  }
+  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                     : launch_one<64, true, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
+             : launch_one<64, false, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
+}
+
+// The instance with the fewest pages per task that holds one split: a task
+// issues loads for all of its instance's pages, so a short split run by the
+// 16-page instance would spend most of its loads on repeats.
 template <bool FUSEDQ>
 static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                            int max_wg) {
-  constexpr int DP = KVPAGE_ATTN_DEPTH;
-  const bool bf = s.dtype == KVPAGE_BF16;
-  if (s.d == 128) {
-    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                       : launch_one<128, true, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
-    return bud ? launch_one<128, false, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
-               : launch_one<128, false, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
-  }
-  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                     : launch_one<64, true, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
-  return bud ? launch_one<64, false, true, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg)
-             : launch_one<64, false, false, DP, FUSEDQ>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  const int pages = s.split_tokens / kPage;
+  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return dispatch_ppt<FUSEDQ, 16>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 // Fused queue build: B <= 64 sequences (one lane each in the task lookup).
