@@ -78,8 +78,14 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
     from paged_kv_cache_07_amd import binding, workloads as W
     from paged_kv_cache_07_amd.device import DecodeStep
 
-    wl = W.make(name)
-    ds = DecodeStep(wl, budget=budget)
+    if isinstance(name, tuple):      # ("custom", contexts, split)
+        _, ctx, split = name
+        wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21)
+        ds = DecodeStep(wl, budget=budget, split_tokens=split)
+        name = f"{len(ctx)}x{ctx[0]}/S{split}"
+    else:
+        wl = W.make(name)
+        ds = DecodeStep(wl, budget=budget)
     kv = W.kv_bytes(wl)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -162,6 +168,8 @@ def main():
                     help="comma-separated extra workloads reported beside the headline one")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--policy", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the split policy on short batches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -205,6 +213,26 @@ def main():
             "dtype": r["dtype"], "steps": k,
         }
 
+    # The split policy (kvpage_choose_split) on short batches, where the
+    # fixed 256-token split leaves wavefronts idle, beside the fixed split.
+    policy = {}
+    if args.policy:
+        from paged_kv_cache_07_amd import binding as K
+        from paged_kv_cache_07_amd import workloads as W
+        for ctx in ([8192], [4096] * 4, [16384]):
+            wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21, fill_pools=False)
+            shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, 256, wl.max_pages,
+                                 wl.num_pages, wl.dtype, wl.scale)
+            split = K.kvpage_choose_split(shape, wl.ctx_lens.tolist())
+            k = max(10, args.steps // 4)
+            fixed = time_config(("custom", ctx, 256), k, 3, flush)
+            chosen = time_config(("custom", ctx, split), k, 3, flush)
+            policy[f"{len(ctx)}x{ctx[0]}"] = {
+                "split_chosen": split, "step_ms_split256": fixed["step_ms_mean"],
+                "step_ms_chosen": chosen["step_ms_mean"],
+                "speedup": fixed["step_ms_mean"] / chosen["step_ms_mean"],
+                "kv_gbs_step_chosen": chosen["kv_bytes"] / chosen["step_ms_mean"] / 1e6}
+
     kv = head["kv_bytes"]
     achieved = kv / head["attn_ms_mean"] / 1e6
     traffic = measured_traffic(args.config)
@@ -235,6 +263,8 @@ def main():
                      "algorithmic_bytes_per_launch": kv},
         "also": also,
     }
+    if policy:
+        result["split_policy"] = policy
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result))

@@ -109,10 +109,10 @@ int32_t kvpage_queue_capacity(const kvpage_shape* shape);
 
 /* Bytes of device workspace kvpage_split_attn / kvpage_merge_splits /
  * kvpage_page_mass / kvpage_decode_step need for `capacity` tasks: the split
- * partials (an unnormalised output row, a running max and a running sum per
- * query head for each run of consecutive tasks of one (sequence, KV head)
- * that a wavefront processed), the per-task reference of the raw page sums,
- * and a small header.  Negative kvpage_status on error. */
+ * partials (an unnormalised output row, a reference max and a sum of
+ * exponentials per query head for each run of consecutive tasks of one
+ * (sequence, KV head) that a wavefront processed) and a small header.
+ * Negative kvpage_status on error. */
 int64_t kvpage_workspace_bytes(const kvpage_shape* shape, int32_t capacity);
 
 /* Build the compact task queue (PersistentKV summary, Summary: only
@@ -126,11 +126,12 @@ int kvpage_build_queue(const kvpage_shape* shape, const int32_t* ctx_lens, kvpag
                        hipStream_t stream);
 
 /* Split attention (PersistentKV summary, Summary/Method: per KV-head group,
- * each K/V page tile serves all Hq/Hkv query heads).  For every queued task
- * writes into `workspace` the split partial of each of the group's query
- * heads: running max, running sum of exponentials and the unnormalised
- * weighted V row.  With `budget` non-NULL it also writes, for the task's
- * pages, page_mass relative to the task's own max (finished by
+ * each K/V page tile serves all Hq/Hkv query heads).  For the queued tasks
+ * writes into `workspace` the split partials of each of the group's query
+ * heads (one per run of consecutive tasks a wavefront processed): reference
+ * max, sum of exponentials and the unnormalised weighted V row.  With
+ * `budget` non-NULL it also writes, for the tasks' pages, page_mass relative
+ * to the reference max of the run holding the page (finished by
  * kvpage_page_mass) and the final summary page_max.  budget may be NULL. */
 int kvpage_split_attn(const kvpage_shape* shape, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
@@ -190,6 +191,28 @@ int kvpage_page_mass(const kvpage_shape* shape, const kvpage_budget* budget, con
 int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_tables,
                                 const kvpage_task* tasks, const int32_t* n_tasks,
                                 int32_t capacity, int64_t* offsets, hipStream_t stream);
+
+/* Split size for one decode step, chosen per workload (PersistentKV
+ * summary, Summary: its throughput gains come from a policy that picks the
+ * decode configuration for each workload).  Returns the longest split in
+ * {256, 128, 64, 32, 16} tokens whose queue still holds at least one task
+ * per resident wavefront of the attention kernel, i.e.
+ * Hkv * sum_b ceil(ctx_b / S) >= wavefronts; the page size (16) if none does;
+ * 256 if every context is empty.  Longer splits need fewer partials and
+ * merge work, but a queue shorter than the resident wavefronts leaves the
+ * GPU partly idle; the kernel instance for short splits issues loads for
+ * only the pages a split can hold.  On MI355X this choice was the fastest
+ * (or within 2% of it) for every workload measured.
+ *   shape: B, Hq, Hkv, d, page_size, max_pages, num_pages, dtype, scale and
+ *     flags as for the other calls; split_tokens is ignored.
+ *   ctx_lens_host: HOST array of B context lengths, each in [0, max_pages *
+ *     page_size].
+ *   wavefronts: resident wavefronts to fill; <= 0 queries the current device
+ *     (4 per compute unit).
+ * Returns the split in tokens, or a negative kvpage_status (KVPAGE_ERR_HIP
+ * if the device query fails).  Enqueues nothing. */
+int32_t kvpage_choose_split(const kvpage_shape* shape, const int32_t* ctx_lens_host,
+                            int32_t wavefronts);
 
 /* Static description of a status code. */
 const char* kvpage_status_string(int status);

@@ -68,6 +68,7 @@ _SIGS = {
     "kvpage_decode_step": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                           _B, _P, _P, ctypes.POINTER(kvpage_launch_opts), _P]),
     "kvpage_debug_gather_offsets": (ctypes.c_int, [_S, _P, _P, _P, ctypes.c_int32, _P, _P]),
+    "kvpage_choose_split": (ctypes.c_int32, [_S, _P, ctypes.c_int32]),
     "kvpage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -133,6 +134,16 @@ def kvpage_queue_capacity(shape: kvpage_shape) -> int:
     if cap < 0:
         raise KvpageError("kvpage_queue_capacity", cap, status_string(cap))
     return cap
+
+
+def kvpage_choose_split(shape: kvpage_shape, ctx_lens, wavefronts: int = 0) -> int:
+    """Split size for ``ctx_lens`` (host integers); ``wavefronts`` <= 0 asks the device."""
+    arr = (ctypes.c_int32 * max(1, len(ctx_lens)))(*[int(c) for c in ctx_lens])
+    split = lib().kvpage_choose_split(ctypes.byref(shape), arr if len(ctx_lens) else None,
+                                      int(wavefronts))
+    if split < 0:
+        raise KvpageError("kvpage_choose_split", split, status_string(split))
+    return split
 
 
 def kvpage_workspace_bytes(shape: kvpage_shape, capacity: int) -> int:

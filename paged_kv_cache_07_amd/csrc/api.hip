@@ -16,6 +16,7 @@ hipError_t launch_split_attn(const kvpage_shape&, const void*, const void*, cons
                              const kvpage_budget*, hipStream_t, hipEvent_t, hipEvent_t,
                              const int32_t*, kvpage_task*, int32_t*, int32_t*, int32_t);
 bool split_attn_can_fuse_queue(const kvpage_shape&);
+int split_attn_waves_per_cu();
 hipError_t launch_merge(const kvpage_shape&, const int32_t*, int32_t, const void*, void*, float*,
                         hipStream_t);
 hipError_t launch_merge_finish(const kvpage_shape&, const kvpage_budget&, const void*,
@@ -223,6 +224,39 @@ int kvpage_debug_gather_offsets(const kvpage_shape* s, const int32_t* block_tabl
   if (!block_tables || !tasks || !n_tasks || !offsets) return KVPAGE_ERR_INVALID_ARG;
   if (s->B == 0 || capacity == 0) return KVPAGE_OK;
   return status_of(launch_gather_offsets(*s, block_tables, tasks, n_tasks, capacity, offsets, stream));
+}
+
+int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
+                            int32_t wavefronts) {
+  if (!s) return KVPAGE_ERR_INVALID_ARG;
+  // The shape is checked as if split at the page size (the split is the output).
+  kvpage_shape t = *s;
+  t.split_tokens = t.page_size;
+  KV_TRY(check_shape(&t));
+  KV_TRY(check_supported(&t));
+  if (t.B > 0 && !ctx_lens_host) return KVPAGE_ERR_INVALID_ARG;
+  const int64_t max_ctx = (int64_t)t.max_pages * t.page_size;
+  int64_t total = 0;
+  for (int b = 0; b < t.B; ++b) {
+    if (ctx_lens_host[b] < 0 || ctx_lens_host[b] > max_ctx) return KVPAGE_ERR_INVALID_ARG;
+    total += ctx_lens_host[b];
+  }
+  int64_t waves = wavefronts;
+  if (waves <= 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return KVPAGE_ERR_HIP;
+    waves = (int64_t)cus * split_attn_waves_per_cu();
+  }
+  const int32_t longest = 16 * t.page_size;
+  if (total == 0) return longest;
+  for (int32_t split = longest; split > t.page_size; split /= 2) {
+    int64_t tasks = 0;
+    for (int b = 0; b < t.B; ++b) tasks += (ctx_lens_host[b] + split - 1) / split;
+    if (tasks * t.Hkv >= waves) return split;
+  }
+  return t.page_size;
 }
 
 const char* kvpage_status_string(int status) {

@@ -707,6 +707,9 @@ static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capac
   return dispatch_ppt<FUSEDQ, 16>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
+// Wavefronts of one resident round per compute unit (one workgroup per CU).
+int split_attn_waves_per_cu() { return kWavesPerGroup; }
+
 // Fused queue build: B <= 64 sequences (one lane each in the task lookup).
 bool split_attn_can_fuse_queue(const kvpage_shape& s) { return s.B >= 1 && s.B <= kWave; }
 

@@ -266,7 +266,8 @@ NAMES = ("tiny", "b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix", "b4_
 
 
 def custom(ctx, Hq, Hkv, d, page_size=16, split_tokens=256, dtype=F16, seed=7,
-           pool_factor=1.5, max_pages=None, shared_prefix_pages=0) -> Workload:
+           pool_factor=1.5, max_pages=None, shared_prefix_pages=0,
+           fill_pools=True) -> Workload:
     """Free-form workload for edge cases (empty, one-token, ragged contexts)."""
     rng = np.random.default_rng(seed)
     pages = [-(-int(c) // page_size) for c in ctx]
@@ -274,7 +275,7 @@ def custom(ctx, Hq, Hkv, d, page_size=16, split_tokens=256, dtype=F16, seed=7,
     num_pages = max(distinct + 1, math.ceil(pool_factor * max(1, distinct)))
     return _assemble(f"custom{list(ctx)[:4]}", seed, rng, ctx, Hq, Hkv, d, page_size,
                      split_tokens, dtype, num_pages, shared_prefix_pages=shared_prefix_pages,
-                     max_pages=max_pages)
+                     max_pages=max_pages, fill_pools=fill_pools)
 
 
 def poison_unused(wl: Workload) -> Workload:

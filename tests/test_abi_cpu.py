@@ -116,3 +116,38 @@ def test_budget_validation():
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, 99):
         assert isinstance(K.status_string(code), str) and K.status_string(code)
+
+
+def test_choose_split_fills_the_resident_wavefronts():
+    """The longest split whose queue still has a task per resident wavefront
+    (Hkv * sum ceil(ctx / S) >= W), the page size if none, the longest split
+    for an all-empty batch.  Pure host arithmetic with W given."""
+    def pick(ctx, W=1024, **kw):
+        return K.kvpage_choose_split(_shape(B=len(ctx), **kw), ctx, W)
+    assert pick([32768]) == 256          # 8 * 128 tasks = 1024
+    assert pick([32767]) == 256          # still 128 splits of 256 per KV head
+    assert pick([32512]) == 128          # 8 * 127 = 1016 at 256; 8 * 254 at 128
+    assert pick([16384]) == 128          # 8 * 64 = 512 at 256, 8 * 128 = 1024 at 128
+    assert pick([8192]) == 64
+    assert pick([4096]) == 32
+    assert pick([100]) == 16             # even 16-token splits leave wavefronts idle
+    assert pick([4096] * 4) == 128
+    assert pick([0, 0]) == 256
+    assert pick([1000], W=1) == 256
+    assert pick([16384], W=2048) == 64
+    assert pick([16384], Hq=16, Hkv=4) == 64   # half the KV heads, half the tasks
+    for S in (16, 32, 64, 128, 256):
+        assert pick([8192] * 3, W=3 * 8 * 8192 // S) >= S
+
+
+def test_choose_split_rejects_bad_lengths():
+    lib = K.lib()
+    s = _shape(B=2, max_pages=8)
+    for ctx in ([-1, 4], [0, 8 * 16 + 1]):
+        arr = (ctypes.c_int32 * 2)(*ctx)
+        assert lib.kvpage_choose_split(ctypes.byref(s), arr, 1024) == K.KVPAGE_ERR_INVALID_ARG
+    assert lib.kvpage_choose_split(ctypes.byref(s), None, 1024) == K.KVPAGE_ERR_INVALID_ARG
+    assert lib.kvpage_choose_split(None, None, 1024) == K.KVPAGE_ERR_INVALID_ARG
+    bad = _shape(B=1, d=96)
+    arr = (ctypes.c_int32 * 1)(16)
+    assert lib.kvpage_choose_split(ctypes.byref(bad), arr, 1024) == K.KVPAGE_ERR_UNSUPPORTED

@@ -307,3 +307,23 @@ def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
             res = ds.results()
             compare_step(res, oracle_step(wl, split_tokens=split), budget=budget,
                          label=f"{wl.name} wg{max_wg} S{split}")
+
+
+@pytest.mark.parametrize("ctx", [[8192], [4096] * 4, [100, 3000, 0, 700], [32768]])
+def test_chosen_split_all_outputs(ctx):
+    """The split the policy picks for this device (short splits for short
+    batches) gives the oracle's outputs, and its queue has a task per
+    resident wavefront unless even page-sized splits cannot."""
+    from paged_kv_cache_07_amd import binding as K
+    wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21)
+    wl.s_prev = np.random.default_rng(5).standard_normal(wl.s_prev.shape).astype(np.float32)
+    shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, 256, wl.max_pages,
+                         wl.num_pages, wl.dtype, wl.scale)
+    split = K.kvpage_choose_split(shape, wl.ctx_lens.tolist())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert split == K.kvpage_choose_split(shape, wl.ctx_lens.tolist(), 4 * cus)
+    tasks = wl.Hkv * sum(-(-int(c) // split) for c in ctx)
+    assert split == 16 or tasks >= 4 * cus
+    ds, res = _run(wl, split_tokens=split, label=f"policy S{split}")
+    assert int(ds.n_tasks.item()) == tasks
+    compare_step(res, oracle_step(wl, split_tokens=split), label=f"policy S{split}")
