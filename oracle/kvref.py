@@ -22,6 +22,12 @@ What is computed, and where it comes from:
 * Page mass -- the per-page sum of the softmax weights of the step, the
   page-level attention signal that GrowPage's page budgeting consumes
   (mlsanity.com GrowPage entry, Abstract: page-level KV abstraction).
+* KV append -- the step before attention: each sequence's new token goes to
+  slot ``ctx % P`` of its last page; a sequence at a page boundary first takes
+  a physical page from the pool's integer free list (GrowPage, aitrending.vip
+  article, Technical Details: a page is acquired at a capacity boundary;
+  "Elastic KV Cache for LLM Serving", 2 Background and Motivation: the paged
+  pool is fixed-size blocks handed out from an integer free list).
 * Query summaries -- GrowPage (Abstract; aitrending.vip article, Technical
   Details) keeps dual-timescale query summaries.  Here: per (sequence, KV
   group) a fast and a slow exponential moving average of the group-mean query,
@@ -40,8 +46,12 @@ import numpy as np
 
 __all__ = [
     "widen", "build_queue", "gather_offsets", "logical_rows", "attention",
-    "update_summaries", "summary_page_max", "decode_step",
+    "update_summaries", "summary_page_max", "decode_step", "append_kv",
+    "APPEND_FULL", "APPEND_NO_PAGE",
 ]
+
+APPEND_FULL = 1      # status bit: a sequence had no room left in its block-table row
+APPEND_NO_PAGE = 2   # status bit: the free list ran out
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -211,3 +221,48 @@ def decode_step(wl, rows=None, q=None, s_prev=None):
                           wl.scale, wl.dtype, groups=groups)
     return {"tasks": tasks, "group_offsets": offsets, "n_tasks": n, "out": out,
             "lse": lse, "mass": mass, "s_next": s_next, "page_max": pm}
+
+
+def append_kv(k_pool, v_pool, block_tables, ctx_lens, k_new, v_new, free_pages, free_count,
+              page_size: int):
+    """Append one token per sequence to the paged cache (see the header).
+
+    Sequences are taken in order.  Sequence ``b`` with ``t = ctx_lens[b]``:
+
+    * ``t == max_pages * P``: its row is full; nothing changes for it and the
+      status gets ``APPEND_FULL``.
+    * ``t % P == 0``: it needs a new page.  The k-th sequence (in order)
+      needing one takes ``free_pages[free_count - 1 - k]`` (the top of the
+      stack) and records it at ``block_tables[b, t // P]``; if ``k >=
+      free_count`` the list is exhausted: nothing changes for it and the
+      status gets ``APPEND_NO_PAGE``.
+    * Otherwise its page is ``block_tables[b, t // P]``.
+
+    Then ``k_new[b, g]`` / ``v_new[b, g]`` are written to slot ``t % P`` of
+    that page for every KV head ``g``, and its length becomes ``t + 1``.
+
+    Returns new copies ``(k_pool, v_pool, block_tables, ctx_lens, free_count,
+    status)``; inputs are not modified.  Pure integer and copy work: the
+    pools keep their dtype and bits.
+    """
+    k_pool, v_pool = k_pool.copy(), v_pool.copy()
+    bt = np.array(block_tables, dtype=np.int32, copy=True)
+    ctx = np.array(ctx_lens, dtype=np.int32, copy=True)
+    max_pages = bt.shape[1]
+    taken, status = 0, 0
+    for b in range(len(ctx)):
+        t = int(ctx[b])
+        if t >= max_pages * page_size:
+            status |= APPEND_FULL
+            continue
+        if t % page_size == 0:
+            if taken >= free_count:
+                status |= APPEND_NO_PAGE
+                continue
+            bt[b, t // page_size] = free_pages[free_count - 1 - taken]
+            taken += 1
+        page = int(bt[b, t // page_size])
+        k_pool[page, :, t % page_size, :] = k_new[b]
+        v_pool[page, :, t % page_size, :] = v_new[b]
+        ctx[b] = t + 1
+    return k_pool, v_pool, bt, ctx, free_count - taken, status

@@ -351,3 +351,73 @@ def test_bf16_widening_is_exact():
     back = kvref.widen(bits, "bf16")
     assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -8)
     assert kvref.widen(np.array([0x3F80], dtype=np.uint16), "bf16")[0] == 1.0
+
+
+# ------------------------------------------------------------- KV append ---
+
+def _read_append_golden():
+    kv = {}
+    for line in open(os.path.join(GOLDEN, "append_small.txt")):
+        if line.strip() and not line.startswith("#"):
+            key, *vals = line.split()
+            kv[key] = vals
+    rows = lambda v: np.array([[int(x) for x in r.split(",")] for r in v], dtype=np.int32)
+    ints = lambda v: np.array([int(x) for x in v], dtype=np.int32)
+    return kv, rows, ints
+
+
+def test_append_golden_hand_worked():
+    kv, rows, ints = _read_append_golden()
+    P, npages, Hkv, d = int(kv["page_size"][0]), int(kv["num_pages"][0]), 2, 8
+    table = rows(kv["table"])
+    ctx = ints(kv["ctx_in"])
+    B = len(ctx)
+    k_pool = np.zeros((npages, Hkv, P, d), np.float16)
+    v_pool = np.zeros((npages, Hkv, P, d), np.float16)
+    k_new = (1 + np.arange(B * Hkv * d, dtype=np.float16).reshape(B, Hkv, d))
+    v_new = -k_new
+    k2, v2, t2, c2, fc2, st = kvref.append_kv(k_pool, v_pool, table, ctx, k_new, v_new,
+                                               ints(kv["free_pages"]), int(kv["free_count"][0]), P)
+    assert np.array_equal(c2, ints(kv["ctx_out"]))
+    assert fc2 == int(kv["free_count_out"][0])
+    assert st == int(kv["status"][0]) == kvref.APPEND_FULL | kvref.APPEND_NO_PAGE
+    assert np.array_equal(t2, rows(kv["table_out"]))
+    want_k = np.zeros_like(k_pool)
+    want_v = np.zeros_like(v_pool)
+    for w in kv["written"]:
+        b, page, slot = (int(x) for x in w.split(":"))
+        want_k[page, :, slot, :] = k_new[b]
+        want_v[page, :, slot, :] = v_new[b]
+    assert np.array_equal(k2, want_k) and np.array_equal(v2, want_v)
+    # inputs untouched
+    assert np.array_equal(table, rows(kv["table"])) and not k_pool.any()
+
+
+def test_append_then_gather_reads_the_new_token():
+    """On a random paged cache: after the append, logical token ctx_b of every
+    appended sequence is the new K/V (read back through the pinned gather), all
+    earlier tokens are unchanged, and the pages taken are the top of the free
+    list in sequence order, each used once."""
+    wl = W.custom([0, 16, 17, 31, 32, 90, 47, 64], Hq=4, Hkv=2, d=16, seed=3, max_pages=6)
+    rng = np.random.default_rng(9)
+    free = np.setdiff1d(np.arange(wl.num_pages), wl.block_tables[wl.block_tables < wl.num_pages])
+    free = rng.permutation(free).astype(np.int32)
+    k_new = rng.standard_normal((wl.B, wl.Hkv, wl.d)).astype(np.float16)
+    v_new = rng.standard_normal((wl.B, wl.Hkv, wl.d)).astype(np.float16)
+    k2, v2, bt2, c2, fc2, st = kvref.append_kv(wl.k_pool, wl.v_pool, wl.block_tables, wl.ctx_lens,
+                                                k_new, v_new, free, len(free), wl.page_size)
+    need = [b for b, c in enumerate(wl.ctx_lens) if c % 16 == 0 and c < 6 * 16]
+    assert st == 0 and fc2 == len(free) - len(need)
+    for k, b in enumerate(need):
+        assert bt2[b, wl.ctx_lens[b] // 16] == free[len(free) - 1 - k]
+    assert np.array_equal(c2, wl.ctx_lens + 1)
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            old = kvref.logical_rows(wl.k_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, "f16")
+            new = kvref.logical_rows(k2, bt2, b, g, int(c2[b]), 16, "f16")
+            assert np.array_equal(new[:-1], old) and np.array_equal(new[-1], k_new[b, g].astype(np.float64))
+            newv = kvref.logical_rows(v2, bt2, b, g, int(c2[b]), 16, "f16")
+            assert np.array_equal(newv[-1], v_new[b, g].astype(np.float64))
+    # Only the appended slots changed in the pools.
+    changed = np.argwhere(np.any(k2 != wl.k_pool, axis=-1))
+    assert len(changed) <= wl.B * wl.Hkv
