@@ -47,11 +47,12 @@ import numpy as np
 __all__ = [
     "widen", "build_queue", "gather_offsets", "logical_rows", "attention",
     "update_summaries", "summary_page_max", "decode_step", "append_kv",
-    "APPEND_FULL", "APPEND_NO_PAGE",
+    "APPEND_FULL", "APPEND_NO_PAGE", "APPEND_BAD_PAGE",
 ]
 
 APPEND_FULL = 1      # status bit: a sequence had no room left in its block-table row
 APPEND_NO_PAGE = 2   # status bit: the free list ran out
+APPEND_BAD_PAGE = 4  # status bit: a page id outside the pool (free list or table)
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -237,6 +238,9 @@ def append_kv(k_pool, v_pool, block_tables, ctx_lens, k_new, v_new, free_pages, 
       free_count`` the list is exhausted: nothing changes for it and the
       status gets ``APPEND_NO_PAGE``.
     * Otherwise its page is ``block_tables[b, t // P]``.
+    * A page id outside ``[0, num_pages)`` leaves the sequence unchanged (a
+      free-list entry it came from is still used up) and sets
+      ``APPEND_BAD_PAGE``.
 
     Then ``k_new[b, g]`` / ``v_new[b, g]`` are written to slot ``t % P`` of
     that page for every KV head ``g``, and its length becomes ``t + 1``.
@@ -255,13 +259,20 @@ def append_kv(k_pool, v_pool, block_tables, ctx_lens, k_new, v_new, free_pages, 
         if t >= max_pages * page_size:
             status |= APPEND_FULL
             continue
-        if t % page_size == 0:
+        new_page = t % page_size == 0
+        if new_page:
             if taken >= free_count:
                 status |= APPEND_NO_PAGE
                 continue
-            bt[b, t // page_size] = free_pages[free_count - 1 - taken]
+            page = int(free_pages[free_count - 1 - taken])
             taken += 1
-        page = int(bt[b, t // page_size])
+        else:
+            page = int(bt[b, t // page_size])
+        if not 0 <= page < k_pool.shape[0]:
+            status |= APPEND_BAD_PAGE
+            continue
+        if new_page:
+            bt[b, t // page_size] = page
         k_pool[page, :, t % page_size, :] = k_new[b]
         v_pool[page, :, t % page_size, :] = v_new[b]
         ctx[b] = t + 1

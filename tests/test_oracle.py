@@ -421,3 +421,17 @@ def test_append_then_gather_reads_the_new_token():
     # Only the appended slots changed in the pools.
     changed = np.argwhere(np.any(k2 != wl.k_pool, axis=-1))
     assert len(changed) <= wl.B * wl.Hkv
+
+
+def test_append_bad_page_ids_change_nothing_for_that_sequence():
+    kv, rows, ints = _read_append_golden()
+    P = 16
+    k_pool = np.zeros((16, 1, P, 8), np.float16)
+    table = np.array([[3, 15], [99, 15], [4, 15]], np.int32)   # row 1 points outside the pool
+    ctx = np.array([5, 7, 16], np.int32)
+    free = np.array([-1], np.int32)                             # seq 2 would take page -1
+    k_new = np.ones((3, 1, 8), np.float16)
+    k2, _, t2, c2, fc2, st = kvref.append_kv(k_pool, k_pool, table, ctx, k_new, k_new, free, 1, P)
+    assert st == kvref.APPEND_BAD_PAGE
+    assert np.array_equal(c2, [6, 7, 16]) and fc2 == 0 and np.array_equal(t2, table)
+    assert k2[3, 0, 5].all() and k2.sum() == 8
