@@ -214,6 +214,45 @@ int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_
 int32_t kvpage_choose_split(const kvpage_shape* shape, const int32_t* ctx_lens_host,
                             int32_t wavefronts);
 
+/* Status bits kvpage_append_kv writes to its device status word. */
+enum {
+  KVPAGE_APPEND_FULL = 1,      /* a sequence's block-table row had no room left */
+  KVPAGE_APPEND_NO_PAGE = 2,   /* the free list ran out */
+  KVPAGE_APPEND_BAD_PAGE = 4   /* a page id outside [0, num_pages) in the free list or a table */
+};
+
+/* Append one token per sequence to the paged cache, the step before decode
+ * attention (GrowPage, aitrending.vip article, Technical Details: a physical
+ * page is acquired at a capacity boundary; "Elastic KV Cache for LLM
+ * Serving", 2 Background and Motivation: fixed-size KV blocks handed out from
+ * an integer free list).  For sequence b, in order, with t = ctx_lens[b]:
+ *   t == max_pages * page_size: nothing changes for b (KVPAGE_APPEND_FULL);
+ *   t % page_size == 0: b needs a page.  The k-th such sequence takes
+ *     free_pages[*free_count - 1 - k] (the top of the stack) and records it in
+ *     block_tables[b, t / page_size]; if k >= *free_count nothing changes for
+ *     b (KVPAGE_APPEND_NO_PAGE);
+ *   otherwise its page is block_tables[b, t / page_size].
+ * A page id outside [0, num_pages) leaves b unchanged (a free-list entry it
+ * came from is still used up; KVPAGE_APPEND_BAD_PAGE).  Then k_new[b, g, :]
+ * and v_new[b, g, :] go to slot t % page_size of that page for every KV head
+ * g, and ctx_lens_out[b] = t + 1 (t when b was left unchanged).
+ *   k_new, v_new: [B, Hkv, d] in the pools' dtype, device.
+ *   k_pool, v_pool, block_tables: updated in place, device.
+ *   ctx_lens (read) and ctx_lens_out (written): [B] int32, device, must not
+ *     overlap.  Lengths must lie in [0, max_pages * page_size].
+ *   free_pages: [*free_count] int32, device; free_count (read) and
+ *     free_count_out (written, = free_count minus the pages taken): one int32
+ *     each, device, must not overlap.
+ *   status: one int32, device, written with the KVPAGE_APPEND_* bits (0 when
+ *     every sequence was appended).
+ * shape: B, Hkv, d, page_size, max_pages, num_pages and dtype are used; the
+ * other fields are checked as for the other calls.  Negative kvpage_status on
+ * invalid arguments (nothing enqueued). */
+int kvpage_append_kv(const kvpage_shape* shape, const void* k_new, const void* v_new,
+                     void* k_pool, void* v_pool, int32_t* block_tables, const int32_t* ctx_lens,
+                     int32_t* ctx_lens_out, const int32_t* free_pages, const int32_t* free_count,
+                     int32_t* free_count_out, int32_t* status, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kvpage_status_string(int status);
 

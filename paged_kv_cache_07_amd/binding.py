@@ -69,6 +69,7 @@ _SIGS = {
                                           _B, _P, _P, ctypes.POINTER(kvpage_launch_opts), _P]),
     "kvpage_debug_gather_offsets": (ctypes.c_int, [_S, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "kvpage_choose_split": (ctypes.c_int32, [_S, _P, ctypes.c_int32]),
+    "kvpage_append_kv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kvpage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -144,6 +145,17 @@ def kvpage_choose_split(shape: kvpage_shape, ctx_lens, wavefronts: int = 0) -> i
     if split < 0:
         raise KvpageError("kvpage_choose_split", split, status_string(split))
     return split
+
+
+KVPAGE_APPEND_FULL, KVPAGE_APPEND_NO_PAGE, KVPAGE_APPEND_BAD_PAGE = 1, 2, 4
+
+
+def kvpage_append_kv(shape, k_new, v_new, k_pool, v_pool, block_tables, ctx_lens, ctx_lens_out,
+                     free_pages, free_count, free_count_out, status, stream=None):
+    return _check("kvpage_append_kv", lib().kvpage_append_kv(
+        ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(ctx_lens_out), _ptr(free_pages),
+        _ptr(free_count), _ptr(free_count_out), _ptr(status), _stream(stream)))
 
 
 def kvpage_workspace_bytes(shape: kvpage_shape, capacity: int) -> int:

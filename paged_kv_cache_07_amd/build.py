@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvpage.so")
-SOURCES = ("api.hip", "queue.hip", "attn.hip", "merge.hip")
+SOURCES = ("api.hip", "queue.hip", "attn.hip", "merge.hip", "append.hip")
 ARCH = "gfx950"
 
 # The packed-FP32 feature is switched off: every float op stays scalar.

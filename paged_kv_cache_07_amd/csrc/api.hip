@@ -16,6 +16,9 @@ hipError_t launch_split_attn(const kvpage_shape&, const void*, const void*, cons
                              const kvpage_budget*, hipStream_t, hipEvent_t, hipEvent_t,
                              const int32_t*, kvpage_task*, int32_t*, int32_t*, int32_t);
 bool split_attn_can_fuse_queue(const kvpage_shape&);
+hipError_t launch_append(const kvpage_shape&, const void*, const void*, void*, void*, int32_t*,
+                         const int32_t*, int32_t*, const int32_t*, const int32_t*, int32_t*,
+                         int32_t*, hipStream_t);
 int split_attn_waves_per_cu();
 hipError_t launch_merge(const kvpage_shape&, const int32_t*, int32_t, const void*, void*, float*,
                         hipStream_t);
@@ -224,6 +227,24 @@ int kvpage_debug_gather_offsets(const kvpage_shape* s, const int32_t* block_tabl
   if (!block_tables || !tasks || !n_tasks || !offsets) return KVPAGE_ERR_INVALID_ARG;
   if (s->B == 0 || capacity == 0) return KVPAGE_OK;
   return status_of(launch_gather_offsets(*s, block_tables, tasks, n_tasks, capacity, offsets, stream));
+}
+
+int kvpage_append_kv(const kvpage_shape* s, const void* k_new, const void* v_new, void* k_pool,
+                     void* v_pool, int32_t* block_tables, const int32_t* ctx_lens,
+                     int32_t* ctx_lens_out, const int32_t* free_pages, const int32_t* free_count,
+                     int32_t* free_count_out, int32_t* status, hipStream_t stream) {
+  KV_TRY(check_shape(s));
+  KV_TRY(check_supported(s));
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !ctx_lens || !ctx_lens_out ||
+      !free_pages || !free_count || !free_count_out || !status)
+    return KVPAGE_ERR_INVALID_ARG;
+  if (ctx_lens == ctx_lens_out || free_count == free_count_out) return KVPAGE_ERR_INVALID_ARG;
+  // 16-byte row copies: the rows of one token are d halves (d is 64 or 128).
+  for (const void* ptr : {k_new, v_new, (const void*)k_pool, (const void*)v_pool})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return KVPAGE_ERR_INVALID_ARG;
+  return status_of(launch_append(*s, k_new, v_new, k_pool, v_pool, block_tables, ctx_lens,
+                                 ctx_lens_out, free_pages, free_count, free_count_out, status,
+                                 stream));
 }
 
 int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,

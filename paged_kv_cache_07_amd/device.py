@@ -119,6 +119,29 @@ class DecodeStep:
                              self.capacity, self.workspace, self.budget, self.out, self.lse,
                              opts, stream)
 
+    # -- KV append (the step before attention) ----------------------------
+    def set_free_list(self, free_pages: np.ndarray):
+        """Physical pages the appends may take (a stack: the last entry goes first)."""
+        torch = _torch()
+        dev = self.device
+        fp = np.ascontiguousarray(free_pages, dtype=np.int32)
+        self.free_pages = torch.from_numpy(fp if len(fp) else np.zeros(1, np.int32)).to(dev)
+        self.free_count = torch.tensor([len(fp)], dtype=torch.int32, device=dev)
+        self.free_count_next = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ctx_next = torch.zeros_like(self.ctx_lens)
+        self.append_status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def append_kv(self, k_new_host: np.ndarray, v_new_host: np.ndarray, stream=None):
+        """Append one token per sequence; the new lengths and free count become current."""
+        k_new = host_to_device(k_new_host, self.wl.dtype, self.device)
+        v_new = host_to_device(v_new_host, self.wl.dtype, self.device)
+        K.kvpage_append_kv(self.shape, k_new, v_new, self.k_pool, self.v_pool, self.block_tables,
+                           self.ctx_lens, self.ctx_next, self.free_pages, self.free_count,
+                           self.free_count_next, self.append_status, stream)
+        self.ctx_lens, self.ctx_next = self.ctx_next, self.ctx_lens
+        self.free_count, self.free_count_next = self.free_count_next, self.free_count
+        self._keep = (k_new, v_new)   # alive until the stream has used them
+
     def gather_offsets(self, stream=None):
         torch = _torch()
         offs = torch.full((max(1, self.capacity), self.split_tokens), -7, dtype=torch.int64,

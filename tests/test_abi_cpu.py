@@ -151,3 +151,26 @@ def test_choose_split_rejects_bad_lengths():
     bad = _shape(B=1, d=96)
     arr = (ctypes.c_int32 * 1)(16)
     assert lib.kvpage_choose_split(ctypes.byref(bad), arr, 1024) == K.KVPAGE_ERR_UNSUPPORTED
+
+
+def test_append_rejects_bad_arguments():
+    """Null pointers, in/out buffers that overlap and misaligned rows are
+    refused on the host (nothing enqueued, no device needed)."""
+    lib = K.lib()
+    s = _shape(B=4)
+    p = [ctypes.c_void_p(256 * (i + 1)) for i in range(11)]
+    ok = lambda args: lib.kvpage_append_kv(ctypes.byref(s), *args, None)
+    for i in range(11):
+        args = list(p)
+        args[i] = None
+        assert ok(args) == K.KVPAGE_ERR_INVALID_ARG, i
+    args = list(p)
+    args[6] = args[5]                      # ctx_lens_out == ctx_lens
+    assert ok(args) == K.KVPAGE_ERR_INVALID_ARG
+    args = list(p)
+    args[9] = args[8]                      # free_count_out == free_count
+    assert ok(args) == K.KVPAGE_ERR_INVALID_ARG
+    args = list(p)
+    args[0] = ctypes.c_void_p(256 + 8)     # k_new not 16-byte aligned
+    assert ok(args) == K.KVPAGE_ERR_INVALID_ARG
+    assert lib.kvpage_append_kv(ctypes.byref(_shape(B=4, d=96)), *p, None) == K.KVPAGE_ERR_UNSUPPORTED
