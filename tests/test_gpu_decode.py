@@ -27,12 +27,17 @@ def _need_gpu():
     binding.lib()
 
 
-def _run(wl, budget=True, split_tokens=None, label=""):
+def _run(wl, budget=True, split_tokens=None, label="", one_call=False):
+    """Separate calls (queue, attention + merge, page-mass finish), or with
+    one_call the single kvpage_decode_step call bench.py times."""
     from paged_kv_cache_07_amd.device import DecodeStep
     say("run", label or wl.name, "ctx", wl.ctx_lens.tolist()[:8], "G", wl.G, "d", wl.d,
-        wl.dtype, "split", split_tokens or wl.split_tokens, "budget", budget)
+        wl.dtype, "split", split_tokens or wl.split_tokens, "budget", budget, "one_call", one_call)
     ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens)
-    ds.run()
+    if one_call:
+        ds.step()
+    else:
+        ds.run()
     return ds, ds.results()
 
 
@@ -146,8 +151,13 @@ def test_oracle_sized_configs_all_outputs(name, div):
 @pytest.mark.parametrize("name", ["b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix",
                                   "b4_bimodal"])
 def test_full_size_sampled_rows(name):
+    """Full-size workloads in the launch configuration bench.py times (one
+    kvpage_decode_step call), sampled rows against the oracle."""
     wl = W.make(name)
-    _, res = _run(wl, label=f"{name}-full")
+    _, res = _run(wl, label=f"{name}-full", one_call=True)
+    tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
+    assert res["n_tasks"] == n
+    assert np.array_equal(res["tasks"], tasks) and np.array_equal(res["group_offsets"], offs)
     rows = sample_rows(wl, 6, seed=3)
     ref = oracle_step(wl, rows=rows)
     compare_step(res, ref, label=name)
