@@ -403,8 +403,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   };
 
   Task cur = fetch(t_first);
-  int32_t ids = load_page_ids(cur);
+  // Query rows first: they arrive with the page ids, so the operand is built
+  // while the first tiles are in flight.
   Rows rows = load_rows(cur);
+  int32_t ids = load_page_ids(cur);
   uint32_t buf[DEPTH][TW];
 #pragma unroll
   for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
