@@ -164,7 +164,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="b1")
-    ap.add_argument("--also", default="b8_bimodal,b8_uniform,b8_zipf,b64_prefix",
+    ap.add_argument("--also", default="b8_bimodal,b8_uniform,b8_zipf,b64_prefix,b4_bimodal",
                     help="comma-separated extra workloads reported beside the headline one")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
