@@ -594,7 +594,20 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         __builtin_amdgcn_wave_barrier();
         if (lane < nk) p.tasks_out[run_start + lane] = lds_task[wave][lane];
       }
-      if constexpr (BUDGET) {
+      if (BUDGET && kin == 0) {
+        // A run of one task: its reference is the run's, so the page values
+        // in registers are final (page 4r + u of head / summary column n).
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int pg = 4 * r + u;
+          if (pg < npg) {
+            if (is_head)
+              p.page_mass[((int64_t)b * p.Hq + (int64_t)g * G + n) * p.max_pages + run_lp0 + pg] = keep[u];
+            if (is_lead)
+              p.page_max[(((int64_t)(n == G ? 0 : 1) * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0 + pg] = keep[u];
+          }
+        }
+      } else if constexpr (BUDGET) {
         // Raw page sums move to the run's final reference, the one its
         // partial carries; pages of a run are consecutive in the sequence.
         __builtin_amdgcn_wave_barrier();
