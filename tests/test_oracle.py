@@ -435,3 +435,37 @@ def test_append_bad_page_ids_change_nothing_for_that_sequence():
     assert st == kvref.APPEND_BAD_PAGE
     assert np.array_equal(c2, [6, 7, 16]) and fc2 == 0 and np.array_equal(t2, table)
     assert k2[3, 0, 5].all() and k2.sum() == 8
+
+
+@pytest.mark.parametrize("split", [16, 32, 64, 256, 1 << 20])
+def test_split_partials_merged_by_lse_equal_the_full_softmax(split):
+    """The method reaches the plain softmax only up to rounding: per queue
+    task (split) a partial max m, sum l and weighted V sum o, merged with the
+    log-sum-exp rule, must give the oracle's out and lse to ~1e-12 (the
+    pages' split-KV decode over the compact queue; the merge is the textbook
+    one).  Computed here from the gathered rows, independently of
+    ``kvref.attention``'s single pass."""
+    wl = W.custom([37, 100, 1, 0, 300], Hq=6, Hkv=2, d=16, seed=17)
+    out, lse, _ = kvref.attention(wl.q, wl.k_pool, wl.v_pool, wl.block_tables, wl.ctx_lens,
+                                  wl.page_size, wl.scale, wl.dtype)
+    tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, split)
+    parts = {}
+    for b, g, t0, t1 in tasks:
+        K = kvref.logical_rows(wl.k_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, wl.dtype)[t0:t1]
+        V = kvref.logical_rows(wl.v_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, wl.dtype)[t0:t1]
+        for h in range(g * wl.G, (g + 1) * wl.G):
+            x = wl.scale * (K @ kvref.widen(wl.q[b, h], wl.dtype))
+            m = x.max()
+            w = np.exp(x - m)
+            parts.setdefault((b, h), []).append((m, w.sum(), w @ V))
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            if wl.ctx_lens[b] == 0:
+                assert (b, h) not in parts and lse[b, h] == -np.inf and not out[b, h].any()
+                continue
+            ps = parts[(b, h)]
+            M = max(p[0] for p in ps)
+            L = sum(np.exp(p[0] - M) * p[1] for p in ps)
+            O = sum(np.exp(p[0] - M) * p[2] for p in ps) / L
+            np.testing.assert_allclose(O, out[b, h], rtol=1e-12, atol=1e-14)
+            assert abs(M + np.log(L) - lse[b, h]) <= 1e-12 * max(1.0, abs(lse[b, h]))
