@@ -337,3 +337,20 @@ def test_chosen_split_all_outputs(ctx):
     ds, res = _run(wl, split_tokens=split, label=f"policy S{split}")
     assert int(ds.n_tasks.item()) == tasks
     compare_step(res, oracle_step(wl, split_tokens=split), label=f"policy S{split}")
+
+
+@pytest.mark.parametrize("budget", [True, False])
+def test_one_call_step_beyond_64_sequences(budget):
+    """More than 64 sequences: kvpage_decode_step builds the queue with its
+    own kernel before the attention kernel (the fused build covers up to 64);
+    100 x 32 rows also take the one-wavefront-per-row merge."""
+    rng = np.random.default_rng(12)
+    ctx = rng.integers(0, 700, 100)
+    ctx[::9] = 0
+    wl = W.custom(ctx.tolist(), Hq=32, Hkv=8, d=128, seed=51)
+    wl.s_prev = rng.standard_normal(wl.s_prev.shape).astype(np.float32)
+    ds, res = _run(wl, budget=budget, label="B100", one_call=True)
+    tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
+    assert res["n_tasks"] == n and np.array_equal(res["tasks"], tasks)
+    assert np.array_equal(res["group_offsets"], offs)
+    compare_step(res, oracle_step(wl), budget=budget, label="B100")
