@@ -354,3 +354,24 @@ def test_one_call_step_beyond_64_sequences(budget):
     assert res["n_tasks"] == n and np.array_equal(res["tasks"], tasks)
     assert np.array_equal(res["group_offsets"], offs)
     compare_step(res, oracle_step(wl), budget=budget, label="B100")
+
+
+@pytest.mark.parametrize("gain", [6.0, 24.0])
+def test_peaky_queries_exercise_run_rescales(gain):
+    """Queries scaled up (scores with standard deviation ~gain): the softmax
+    is dominated by a few tokens, a run's reference max moves often between
+    its tasks, and weights span many orders of magnitude.  Few workgroups so
+    runs are long; both dtypes."""
+    from paged_kv_cache_07_amd import binding
+    from paged_kv_cache_07_amd.device import DecodeStep
+    for dtype, d in (("f16", 128), ("bf16", 64)):
+        wl = W.custom([3000, 517, 1024, 40], Hq=16, Hkv=4, d=d, dtype=dtype, seed=61)
+        q = wl.q.astype(np.float32) if dtype == "f16" else \
+            (wl.q.astype(np.uint32) << 16).view(np.float32)
+        q = q * gain
+        wl.q = q.astype(np.float16) if dtype == "f16" else W.f32_to_bf16_bits(q)
+        for max_wg in (0, 2):
+            say("peaky", gain, dtype, "max_wg", max_wg)
+            ds = DecodeStep(wl, budget=True)
+            ds.step(opts=binding.make_opts(max_workgroups=max_wg))
+            compare_step(ds.results(), oracle_step(wl), label=f"peaky x{gain} {dtype} wg{max_wg}")
