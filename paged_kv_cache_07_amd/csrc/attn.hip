@@ -13,16 +13,19 @@
 //     3 (bf16) pieces that sum to the float32 summary, so the summary-key dot
 //     products (GrowPage: dual-timescale query summaries) cost no extra pass
 //     over K;
-//   * a task (at most 16 pages) runs in two passes: all its scores first,
-//     kept in registers, then the weights exp2(score - task max) and P V, so
-//     the partial carries the task's exact max and nothing is rescaled;
+//   * a task (at most PPT pages, PPT = 4, 8 or 16 by instance) runs in two
+//     passes: all its scores first, kept in LDS, then the weights and P V;
+//   * consecutive tasks of one (sequence, KV head) that a wavefront runs
+//     share one partial whose reference max moves only when a task's max
+//     exceeds it by more than 8 (log2 domain), so weights stay below 2^8;
 //   * P V comes from 16x16x16 MFMAs whose P operand is the score tile's own
 //     register layout, so no lane shuffles are needed between the two
 //     contractions;
 //   * K and V tiles stream through a ring of DEPTH register buffers.
 //
-// Outputs per task go to the workspace: m (log2 domain), l = sum exp2(y - m)
-// and the unnormalised o = sum exp2(y - m) v for each query head of the group.
+// Outputs per run go to the workspace at the run's first queue position:
+// m (log2 domain), l = sum exp2(y - m) and the unnormalised o = sum
+// exp2(y - m) v for each query head of the group.
 #include <float.h>
 #include <math.h>
 
@@ -138,14 +141,14 @@ __device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, bool hi_ha
   return hi_half ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
 }
 
-// One task = pages [0, npg) of one (sequence, KV head) split, npg <= 16.
-// Pass 1 streams the K tiles and keeps every score (16 pages x 4 values per
-// lane); pass 2 streams the V tiles and applies exp2(score - task max), so
-// the task's max is exact and no accumulator is ever rescaled.  Tile loads
-// form one stream (K pages 0..15, then V pages 0..15) fetched DEPTH tiles
-// ahead; loads are issued for all 32 tiles whatever npg is (indices past
-// npg - 1 repeat the last page) so the compiler can count outstanding loads
-// exactly, while computation past npg is skipped.
+// One task = pages [0, npg) of one (sequence, KV head) split, npg <= PPT.
+// Pass 1 streams the K tiles and keeps every score (PPT pages x 4 values per
+// lane, in LDS), so the task's max is exact before any weight is formed;
+// pass 2 streams the V tiles and applies exp2(score - run reference).  Tile
+// loads form one stream (K pages 0..PPT-1, then V pages 0..PPT-1) fetched
+// DEPTH tiles ahead; loads are issued for all 2 * PPT tiles whatever npg is
+// (indices past npg - 1 repeat the last page) so the compiler can count
+// outstanding loads exactly, while computation past npg is skipped.
 // Task lookup for the fused queue build (at most 64 sequences): lane b holds
 // sequence b's split count and the inclusive prefix of task counts, so the
 // (sequence, KV head, split) of queue position t is one ballot away.  This is
