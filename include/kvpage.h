@@ -18,6 +18,11 @@
  *     for a fast and a slow summary of each KV group's queries, the largest
  *     scaled summary-key dot product on every page.
  *
+ * Around the step: kvpage_append_kv is the step before it (append one token
+ * per sequence, taking a page from a free list at a page boundary), and
+ * kvpage_choose_split is a host-side policy that picks the split size for a
+ * batch's context lengths.
+ *
  * Problem statement and data layout (every tensor row-major, contiguous):
  *
  *   q            [B, Hq, d]                     f16 or bf16 (shape.dtype)
