@@ -29,6 +29,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 
 #include "kvpage_common.h"
@@ -654,24 +656,26 @@ template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT>
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
   auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT>;
-  static int blocks_per_cu[64] = {0};
-  static int num_cus[64] = {0};
+  // Resident workgroups of this instance per device, found once.  Concurrent
+  // first calls may both look it up; they store the same value.
+  static std::atomic<int> resident_wg[64];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  const int slot = dev & 63;
-  if (blocks_per_cu[slot] == 0) {
+  std::atomic<int>& cached = resident_wg[dev & 63];
+  int resident_n = cached.load(std::memory_order_relaxed);
+  if (resident_n == 0) {
     int cus = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     int per = 0;
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kWave * kWavesPerGroup, 0);
     if (err != hipSuccess) return err;
-    num_cus[slot] = cus;
-    blocks_per_cu[slot] = per > 0 ? per : 1;
+    resident_n = (per > 0 ? per : 1) * cus;
+    cached.store(resident_n, std::memory_order_relaxed);
   }
   const int64_t want = ((int64_t)capacity + kWavesPerGroup - 1) / kWavesPerGroup;
-  const int64_t resident = (int64_t)blocks_per_cu[slot] * num_cus[slot];
+  const int64_t resident = resident_n;
   int64_t grid64 = want < resident ? want : resident;
   if (max_wg > 0 && grid64 > max_wg) grid64 = max_wg;
   const int grid = (int)grid64;
