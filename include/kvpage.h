@@ -44,6 +44,10 @@
  * work on `stream` and return without synchronizing; the library never
  * allocates, frees or synchronizes and keeps no per-call state.
  *
+ * Alignment: q, k_pool, v_pool and the workspace must be 16-byte aligned,
+ * out 8-byte aligned (vector loads and stores); anything else is
+ * KVPAGE_ERR_INVALID_ARG.
+ *
  * Errors: arguments are validated on the host before anything is enqueued;
  * a failed check returns a negative kvpage_status and enqueues nothing.  A
  * failed kernel launch returns KVPAGE_ERR_HIP.  Data-dependent preconditions

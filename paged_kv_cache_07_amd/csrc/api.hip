@@ -87,6 +87,10 @@ int status_of(hipError_t e) { return e == hipSuccess ? KVPAGE_OK : KVPAGE_ERR_HI
     if (st_ != KVPAGE_OK) return st_; \
   } while (0)
 
+bool aligned(const void* ptr, uintptr_t bytes) {
+  return reinterpret_cast<uintptr_t>(ptr) % bytes == 0;
+}
+
 int validate_attn(const kvpage_shape* s, const void* q, const void* k_pool, const void* v_pool,
                   const int32_t* block_tables, const kvpage_task* tasks, const int32_t* n_tasks,
                   int32_t capacity, const void* workspace, const kvpage_budget* budget) {
@@ -94,6 +98,9 @@ int validate_attn(const kvpage_shape* s, const void* q, const void* k_pool, cons
   KV_TRY(check_supported(s));
   KV_TRY(check_capacity(s, capacity));
   if (!q || !k_pool || !v_pool || !block_tables || !tasks || !n_tasks || !workspace)
+    return KVPAGE_ERR_INVALID_ARG;
+  // 16-byte vector loads of query rows, pool tiles and workspace partials.
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(workspace, 16))
     return KVPAGE_ERR_INVALID_ARG;
   if (budget) KV_TRY(check_budget(budget));
   return KVPAGE_OK;
@@ -151,6 +158,7 @@ int kvpage_merge_splits(const kvpage_shape* s, const int32_t* group_offsets, int
   KV_TRY(check_supported(s));
   KV_TRY(check_capacity(s, capacity));
   if (!group_offsets || !workspace || !out || !lse) return KVPAGE_ERR_INVALID_ARG;
+  if (!aligned(workspace, 16) || !aligned(out, 8)) return KVPAGE_ERR_INVALID_ARG;
   if (s->B == 0) return KVPAGE_OK;
   return status_of(launch_merge(*s, group_offsets, capacity, workspace, out, lse, stream));
 }
@@ -163,6 +171,7 @@ int kvpage_decode_attn(const kvpage_shape* s, const void* q, const void* k_pool,
   KV_TRY(validate_attn(s, q, k_pool, v_pool, block_tables, tasks, n_tasks, capacity, workspace,
                        budget));
   if (!ctx_lens || !group_offsets || !out || !lse) return KVPAGE_ERR_INVALID_ARG;
+  if (!aligned(out, 8)) return KVPAGE_ERR_INVALID_ARG;
   if (s->B == 0) return KVPAGE_OK;
   if (capacity > 0) {
     KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
@@ -180,6 +189,7 @@ int kvpage_decode_step(const kvpage_shape* s, const void* q, const void* k_pool,
   KV_TRY(validate_attn(s, q, k_pool, v_pool, block_tables, tasks, n_tasks, capacity, workspace,
                        budget));
   if (!ctx_lens || !group_offsets || !out || !lse) return KVPAGE_ERR_INVALID_ARG;
+  if (!aligned(out, 8)) return KVPAGE_ERR_INVALID_ARG;
   if (s->B == 0) return KVPAGE_OK;
   hipEvent_t t0 = opts ? opts->attn_start : nullptr;
   hipEvent_t t1 = opts ? opts->attn_stop : nullptr;
@@ -241,7 +251,7 @@ int kvpage_append_kv(const kvpage_shape* s, const void* k_new, const void* v_new
   if (ctx_lens == ctx_lens_out || free_count == free_count_out) return KVPAGE_ERR_INVALID_ARG;
   // 16-byte row copies: the rows of one token are d halves (d is 64 or 128).
   for (const void* ptr : {k_new, v_new, (const void*)k_pool, (const void*)v_pool})
-    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return KVPAGE_ERR_INVALID_ARG;
+    if (!aligned(ptr, 16)) return KVPAGE_ERR_INVALID_ARG;
   return status_of(launch_append(*s, k_new, v_new, k_pool, v_pool, block_tables, ctx_lens,
                                  ctx_lens_out, free_pages, free_count, free_count_out, status,
                                  stream));

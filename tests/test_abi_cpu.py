@@ -174,3 +174,23 @@ def test_append_rejects_bad_arguments():
     args[0] = ctypes.c_void_p(256 + 8)     # k_new not 16-byte aligned
     assert ok(args) == K.KVPAGE_ERR_INVALID_ARG
     assert lib.kvpage_append_kv(ctypes.byref(_shape(B=4, d=96)), *p, None) == K.KVPAGE_ERR_UNSUPPORTED
+
+
+def test_misaligned_buffers_are_rejected():
+    """Vector loads need 16-byte aligned q, pools and workspace and 8-byte
+    aligned out; misaligned pointers are refused on the host."""
+    s = _shape()
+    cap = K.kvpage_queue_capacity(s)
+    lib = K.lib()
+    good = ctypes.c_void_p(4096)
+    for i, bad in ((0, 4096 + 8), (1, 4096 + 4), (2, 4096 + 2), (8, 4096 + 8)):
+        args = [good] * 12
+        args[i] = ctypes.c_void_p(bad)       # q, k_pool, v_pool, workspace
+        rc = lib.kvpage_decode_step(ctypes.byref(s), args[0], args[1], args[2], good, good, good,
+                                    good, good, cap, args[8], None, good, good, None, None)
+        assert rc == K.KVPAGE_ERR_INVALID_ARG, i
+    rc = lib.kvpage_decode_step(ctypes.byref(s), good, good, good, good, good, good, good, good,
+                                cap, good, None, ctypes.c_void_p(4096 + 4), good, None, None)
+    assert rc == K.KVPAGE_ERR_INVALID_ARG           # out
+    assert lib.kvpage_merge_splits(ctypes.byref(s), good, cap, ctypes.c_void_p(4096 + 8), good,
+                                   good, None) == K.KVPAGE_ERR_INVALID_ARG
