@@ -52,9 +52,14 @@
  * a failed check returns a negative kvpage_status and enqueues nothing.  A
  * failed kernel launch returns KVPAGE_ERR_HIP.  Data-dependent preconditions
  * (0 <= ctx_lens[b] <= max_pages * P, 0 <= block-table entries < num_pages
- * for the pages a sequence uses) are the caller's: they are not checked, but
- * every kernel clamps task counts to `capacity` so an inconsistent queue
- * cannot write past the task arrays.
+ * for the pages a sequence uses, queue entries as kvpage_build_queue writes
+ * them) are the caller's and are not reported, but every kernel clamps what
+ * it reads into the shape: lengths to [0, max_pages * P], page ids to
+ * [0, num_pages), queue entries to a sequence, a KV head and at most
+ * split_tokens tokens inside the table row, task counts to `capacity`.  A
+ * violation therefore gives wrong values for the rows it touches and never
+ * an access outside the buffers described here.  (kvpage_append_kv checks
+ * its page ids and lengths and reports them in its status word.)
  */
 #ifndef KVPAGE_H
 #define KVPAGE_H

@@ -107,7 +107,7 @@ struct AttnParams {
   const float* s_prev;
   float* page_max;
   float alpha_fast, alpha_slow;
-  int32_t B, Hq, Hkv, G, max_pages, capacity;
+  int32_t B, Hq, Hkv, G, max_pages, num_pages, capacity;
   float scale, c2, inv_g;
 };
 
@@ -160,9 +160,9 @@ struct SeqScan {
 };
 
 __device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, int Hkv, int S,
-                                                int lane) {
+                                                int max_pages, int lane) {
   SeqScan q;
-  q.ctx = lane < B ? max(ctx_lens[lane], 0) : 0;
+  q.ctx = lane < B ? clamp_ctx(ctx_lens[lane], max_pages) : 0;
   q.ns = (q.ctx + S - 1) / S;
   q.cnt = q.ns * Hkv;
   int v = q.cnt;
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   int ntask;
   SeqScan sq;
   if constexpr (FUSEDQ) {
-    sq = scan_lengths(p.ctx_lens, p.B, p.Hkv, p.split_tokens, lane);
+    sq = scan_lengths(p.ctx_lens, p.B, p.Hkv, p.split_tokens, p.max_pages, lane);
     ntask = min(sq.total, p.capacity);
     if (blockIdx.x == 0 && wave == 0) {
       if (lane < p.B) {
@@ -285,7 +285,14 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       tk.tok_begin = j * p.split_tokens;
       tk.tok_end = min(ctx, tk.tok_begin + p.split_tokens);
     } else {
+      // A caller's queue entry is clamped into the shape: a bad entry gives
+      // wrong values for its row, never an access outside the buffers.
       tk = p.tasks[t];
+      tk.seq = min(max(tk.seq, 0), p.B - 1);
+      tk.kv_head = min(max(tk.kv_head, 0), p.Hkv - 1);
+      tk.tok_begin = clamp_ctx(tk.tok_begin, p.max_pages);
+      tk.tok_end = min(max(tk.tok_end, tk.tok_begin),
+                       min(tk.tok_begin + p.split_tokens, p.max_pages * kPage));
     }
     Task k;
     k.t = t;
@@ -333,8 +340,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   // past npg - 1 repeat the last page (the load count never depends on npg).
   auto load_tile = [&](const Task& k, int32_t ids, int tau, uint32_t (&dst)[TW]) {
     const bool is_v = tau >= PPT;
-    const int pg = min(is_v ? tau - PPT : tau, k.npg - 1);
-    const int32_t pid = __builtin_amdgcn_readlane(ids, pg);
+    const int pg = max(min(is_v ? tau - PPT : tau, k.npg - 1), 0);
+    const int32_t pid = clamp_page(__builtin_amdgcn_readlane(ids, pg), p.num_pages);
     const int64_t off = tile_offset(pid, k.g, p.Hkv, D) * 2;
     if (!is_v) {
       const char* base = kpool + off;
@@ -545,8 +552,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       } else {
         // The next task's first K tiles; with no next task, the same number of
         // loads re-read this task's last V tile (just fetched, so cached).
-        const int pg = has_next ? min(tau + DEPTH - NT, nxt.npg - 1) : npg - 1;
-        const int32_t pid = __builtin_amdgcn_readlane(has_next ? ids_n : ids, pg);
+        const int pg = max(has_next ? min(tau + DEPTH - NT, nxt.npg - 1) : npg - 1, 0);
+        const int32_t pid = clamp_page(__builtin_amdgcn_readlane(has_next ? ids_n : ids, pg), p.num_pages);
         const char* base = (has_next ? kpool : vpool) + tile_offset(pid, has_next ? nxt.g : g, p.Hkv, D) * 2;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -616,10 +623,11 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         // Raw page sums move to the run's final reference, the one its
         // partial carries; pages of a run are consecutive in the sequence.
         __builtin_amdgcn_wave_barrier();
+        const int rp = min(run_pages, p.max_pages - run_lp0);
         for (int h = 0; h < G; ++h) {
           const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), h));
           float* row = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0;
-          for (int pp = lane; pp < run_pages; pp += kWave) {
+          for (int pp = lane; pp < rp; pp += kWave) {
             const int kk = pp / pps;   // task of the run holding page pp
             row[pp] = lds_mass[wave][kk][h][pp - kk * pps] *
                       __builtin_amdgcn_exp2f(lds_tref[wave][kk][h] - mh);
@@ -627,7 +635,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         }
         for (int which = 0; which < 2; ++which) {
           float* row = p.page_max + (((int64_t)which * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0;
-          for (int pp = lane; pp < run_pages; pp += kWave) {
+          for (int pp = lane; pp < rp; pp += kWave) {
             const int kk = pp / pps;
             row[pp] = lds_pmax[wave][kk][which][pp - kk * pps];
           }
@@ -770,6 +778,7 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.Hkv = s.Hkv;
   p.G = G;
   p.max_pages = s.max_pages;
+  p.num_pages = s.num_pages;
   p.capacity = capacity;
   p.scale = s.scale;
   p.c2 = s.scale * 1.4426950408889634f;

@@ -28,6 +28,17 @@ __device__ __forceinline__ int64_t token_offset(const int32_t* bt_row, int32_t t
   return tile_offset(bt_row[t / kPage], kv_head, Hkv, d) + (int64_t)(t % kPage) * d;
 }
 
+// Lengths and page ids come from the caller's device data.  Every kernel
+// clamps them into the shape (a length to [0, max_pages * P], a page id to
+// [0, num_pages)), so a violated precondition gives wrong values for that
+// sequence but no access outside the given buffers.
+__device__ __forceinline__ int32_t clamp_ctx(int32_t ctx, int32_t max_pages) {
+  return min(max(ctx, 0), max_pages * kPage);
+}
+__device__ __forceinline__ int32_t clamp_page(int32_t page, int32_t num_pages) {
+  return min(max(page, 0), num_pages - 1);
+}
+
 // Group-mean query component: heads summed in head order, then scaled by
 // 1/G.  Used by the attention kernel (summary dot products) and by the
 // page-mass kernel (s_next), so both see identical bits.

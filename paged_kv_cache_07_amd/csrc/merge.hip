@@ -91,9 +91,9 @@ __device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pa
   const int lo = p.group_offsets[r.b * p.Hkv + r.g];
   const int hi = p.group_offsets[r.b * p.Hkv + r.g + 1];
   const int runlen = p.ws_hdr[0];
-  const int ctx = need_pages ? p.fin.ctx_lens[r.b] : 0;
-  r.lo = min(lo, p.capacity);
-  r.n = min(hi, p.capacity) - r.lo;
+  const int ctx = need_pages ? clamp_ctx(p.fin.ctx_lens[r.b], p.fin.max_pages) : 0;
+  r.lo = min(max(lo, 0), p.capacity);
+  r.n = max(min(hi, p.capacity) - r.lo, 0);
   r.runlen = max(1, runlen);
   r.nrun = run_count(r.lo, r.lo + r.n, r.runlen);
   r.npg = pages_of(ctx);

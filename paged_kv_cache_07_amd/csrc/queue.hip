@@ -20,15 +20,15 @@ __device__ __forceinline__ int64_t wave_sum(int64_t v) {
 
 // grid = B workgroups of one wave; workgroup b owns sequence b.
 __global__ void __launch_bounds__(kWave) build_queue_kernel(
-    const int32_t* __restrict__ ctx_lens, int32_t B, int32_t Hkv, int32_t S,
+    const int32_t* __restrict__ ctx_lens, int32_t B, int32_t Hkv, int32_t S, int32_t max_pages,
     kvpage_task* __restrict__ tasks, int32_t capacity, int32_t* __restrict__ group_offsets,
     int32_t* __restrict__ n_tasks) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   int64_t before = 0;
-  for (int i = lane; i < b; i += kWave) before += splits_of(ctx_lens[i], S);
+  for (int i = lane; i < b; i += kWave) before += splits_of(clamp_ctx(ctx_lens[i], max_pages), S);
   before = wave_sum(before) * Hkv;
-  const int32_t ctx = ctx_lens[b];
+  const int32_t ctx = clamp_ctx(ctx_lens[b], max_pages);
   const int64_t n_b = splits_of(ctx, S);
   for (int g = lane; g < Hkv; g += kWave) {
     const int64_t off = before + g * n_b;
@@ -59,12 +59,15 @@ __global__ void __launch_bounds__(kWave) build_queue_kernel(
 
 // One workgroup per queued task; lane j covers token slots j, j+64, ...
 __global__ void __launch_bounds__(kWave) gather_offsets_kernel(
-    const int32_t* __restrict__ block_tables, int32_t max_pages, int32_t Hkv, int32_t d,
+    const int32_t* __restrict__ block_tables, int32_t B, int32_t max_pages, int32_t Hkv, int32_t d,
     int32_t S, const kvpage_task* __restrict__ tasks, const int32_t* __restrict__ n_tasks,
     int32_t capacity, int64_t* __restrict__ offsets) {
   const int32_t n = min(n_tasks[0], capacity);
   for (int64_t i = blockIdx.x; i < n; i += gridDim.x) {
-    const kvpage_task t = tasks[i];
+    kvpage_task t = tasks[i];
+    t.seq = min(max(t.seq, 0), B - 1);
+    t.tok_begin = clamp_ctx(t.tok_begin, max_pages);
+    t.tok_end = min(clamp_ctx(t.tok_end, max_pages), t.tok_begin + S);
     const int32_t* bt_row = block_tables + (int64_t)t.seq * max_pages;
     for (int j = threadIdx.x; j < S; j += kWave) {
       const int32_t tok = t.tok_begin + j;
@@ -77,7 +80,7 @@ hipError_t launch_build_queue(const kvpage_shape& s, const int32_t* ctx_lens, kv
                               int32_t capacity, int32_t* group_offsets, int32_t* n_tasks,
                               hipStream_t stream) {
   hipLaunchKernelGGL(build_queue_kernel, dim3(s.B), dim3(kWave), 0, stream, ctx_lens, s.B, s.Hkv,
-                     s.split_tokens, tasks, capacity, group_offsets, n_tasks);
+                     s.split_tokens, s.max_pages, tasks, capacity, group_offsets, n_tasks);
   return hipGetLastError();
 }
 
@@ -86,7 +89,7 @@ hipError_t launch_gather_offsets(const kvpage_shape& s, const int32_t* block_tab
                                  int32_t capacity, int64_t* offsets, hipStream_t stream) {
   const int grid = capacity < 65536 ? capacity : 65536;
   hipLaunchKernelGGL(gather_offsets_kernel, dim3(grid), dim3(kWave), 0, stream, block_tables,
-                     s.max_pages, s.Hkv, s.d, s.split_tokens, tasks, n_tasks, capacity, offsets);
+                     s.B, s.max_pages, s.Hkv, s.d, s.split_tokens, tasks, n_tasks, capacity, offsets);
   return hipGetLastError();
 }
 

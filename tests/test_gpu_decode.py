@@ -375,3 +375,50 @@ def test_peaky_queries_exercise_run_rescales(gain):
             ds = DecodeStep(wl, budget=True)
             ds.step(opts=binding.make_opts(max_workgroups=max_wg))
             compare_step(ds.results(), oracle_step(wl), label=f"peaky x{gain} {dtype} wg{max_wg}")
+
+
+@pytest.mark.parametrize("path", ["one_call", "caller_queue"])
+def test_bad_caller_data_stays_in_its_rows(path):
+    """Page ids outside the pool (sequence 1), a length past the table row
+    (sequence 2), a negative length (sequence 4) and, for a caller's queue,
+    garbage entries in sequence 1's tasks: every kernel clamps what it reads
+    into the shape, so sequences 0 and 3 still match the oracle on the clean
+    data, and the summaries (which need no table) match everywhere."""
+    from paged_kv_cache_07_amd.device import DecodeStep
+    wl = W.custom([300, 200, 500, 77, 1000], Hq=8, Hkv=2, d=64, max_pages=70, seed=23)
+    good = [0, 3]
+    rows = [(b, h) for b in good for h in range(wl.Hq)]
+    ref = oracle_step(wl, rows=rows)
+    bt = wl.block_tables.copy()
+    bt[1, 0:13:2] = wl.num_pages + 7
+    bt[1, 1:13:2] = -5
+    ctx = wl.ctx_lens.copy()
+    ctx[2] = np.iinfo(np.int32).max
+    ctx[4] = -50
+    say("bad-data", path, "num_pages", wl.num_pages, "max_pages", wl.max_pages)
+    ds = DecodeStep(wl)
+    ds.block_tables.copy_(torch.from_numpy(bt))
+    ds.ctx_lens.copy_(torch.from_numpy(ctx))
+    if path == "one_call":
+        ds.step()
+    else:
+        ds.build_queue()
+        n = int(ds.n_tasks.item())
+        tasks = ds.tasks[:n].cpu().numpy().copy()
+        bad = np.flatnonzero(tasks[:, 0] == 1)
+        assert bad.size
+        tasks[bad[0::3]] = [99, -4, -100, 10**9]
+        tasks[bad[1::3]] = [-3, 7, 5000, 4000]
+        tasks[bad[2::3]] = [1, 1, 40, 2**31 - 1]
+        ds.tasks[:n].copy_(torch.from_numpy(tasks))
+        ds.decode_attn()
+        ds.page_mass_finish()
+        ds.gather_offsets()
+    torch.cuda.synchronize()
+    res = ds.results()
+    for b in good:
+        assert_close("out", res["out"][b], ref["out"][b])
+        assert_close("lse", res["lse"][b], ref["lse"][b])
+        assert_close("mass", res["mass"][b], ref["mass"][b])
+        assert_close("page_max", res["page_max"][:, b], ref["page_max"][:, b])
+    assert_close("s_next", res["s_next"], ref["s_next"])
