@@ -44,18 +44,40 @@ struct MergeParams {
   FinishParams fin;
 };
 
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* scratch) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const float o = __shfl_xor(v, off, kWave);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  const int w = threadIdx.x >> 6;
+// Two (max, sum) statistics in the log2 domain combine as m = max(m1, m2),
+// l = l1 2^(m1 - m) + l2 2^(m2 - m); a -inf max carries no mass.
+__device__ __forceinline__ void ml_combine(float& m, float& l, float m2, float l2) {
+  const float nm = fmaxf(m, m2);
+  l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - nm)) +
+      (m2 == -INFINITY ? 0.f : l2 * __builtin_amdgcn_exp2f(m2 - nm));
+  m = nm;
+}
+
+// Workgroup-wide combine of every thread's (m, l): the maximum M, then the
+// sum of l 2^(m - M), each a butterfly per wavefront (a + b == b + a bit for
+// bit, so every lane ends with the same value) followed by the wavefronts'
+// results in wavefront order; every thread returns the same bits.  Called
+// once per kernel (scratch, 2 floats per wavefront, is not reused).  Two
+// plain reductions measured faster than one butterfly over (m, l) pairs,
+// which needs two exponentials per step.
+__device__ __forceinline__ void block_ml(float& m, float& l, float* scratch) {
+  constexpr int NW = kMergeThreads / kWave;
+  const int w = threadIdx.x / kWave;
+  const bool lead = (threadIdx.x & (kWave - 1)) == 0;
+  float v = m;
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  if (lead) scratch[w] = v;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  float M = scratch[0];
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, scratch[i]);
+  float u = m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - M);
+  for (int off = 32; off > 0; off >>= 1) u += __shfl_xor(u, off, kWave);
+  if (lead) scratch[NW + w] = u;
   __syncthreads();
-  float r = scratch[0];
-  for (int i = 1; i < kMergeThreads / kWave; ++i) r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
-  return r;
+  float L = scratch[NW];
+  for (int i = 1; i < NW; ++i) L += scratch[NW + i];
+  m = M;
+  l = L;
 }
 
 template <bool BF>
@@ -65,8 +87,7 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
 }
 
 template <bool BF>
-__device__ __forceinline__ float q_value(const uint16_t* q, int64_t idx) {
-  const uint32_t b16 = q[idx];
+__device__ __forceinline__ float bits_value(uint32_t b16) {
   if constexpr (BF) return __builtin_bit_cast(float, b16 << 16);
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)b16);
 }
@@ -108,28 +129,35 @@ __device__ __forceinline__ int64_t run_index(const MergeParams& p, const Row& r,
   return (int64_t)slot * p.G + r.hh;
 }
 
+// Run statistics (m_j, l_j) of run j = thread, requested with the other
+// loads of the row.  The loads are unconditional (a missing run re-reads the
+// last one and is dropped afterwards): a load under a branch would make the
+// compiler wait for everything in flight before the next use.
+struct StatLoads {
+  float m, l;
+  __device__ __forceinline__ void issue(const MergeParams& p, const Row& r) {
+    const int64_t i = run_index(p, r, threadIdx.x);
+    m = p.ws_rm[i];
+    l = p.ws_rl[i];
+  }
+};
+
 // Log-sum-exp statistics of a row over its run partials: M = max_j m_j and
 // L = sum_j 2^(m_j - M) l_j (log2 domain), in a fixed order, so that every
 // workgroup that needs them gets the same bits.  Returns the natural-log lse
 // exactly as it is stored (-inf for an empty row).
-__device__ float row_lse(const MergeParams& p, const Row& r, float* scratch, float* L_out,
-                         float* M_out) {
-  float tm = -INFINITY, tl = 0.f;
-  for (int j = threadIdx.x; j < max(r.nrun, 1); j += kMergeThreads) {
+__device__ float row_lse(const MergeParams& p, const Row& r, const StatLoads& first,
+                         float* scratch, float* L_out, float* M_out) {
+  float tm = (int)threadIdx.x < r.nrun ? first.m : -INFINITY;
+  float tl = (int)threadIdx.x < r.nrun ? first.l : 0.f;
+  for (int j = threadIdx.x + kMergeThreads; j < r.nrun; j += kMergeThreads) {
     const int64_t i = run_index(p, r, j);
-    const float m = j < r.nrun ? p.ws_rm[i] : -INFINITY;
-    const float l = p.ws_rl[i];
-    const float nm = fmaxf(tm, m);
-    tl = (tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - nm)) +
-         (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - nm));
-    tm = nm;
+    ml_combine(tm, tl, p.ws_rm[i], p.ws_rl[i]);
   }
-  const float M = block_reduce(tm, true, scratch);
-  const float L = block_reduce(tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - M), false,
-                               scratch);
-  *M_out = M;
-  *L_out = L;
-  return r.n > 0 ? (M + log2f(L)) * kLn2 : -INFINITY;
+  block_ml(tm, tl, scratch);
+  *M_out = tm;
+  *L_out = tl;
+  return r.n > 0 ? (tm + log2f(tl)) * kLn2 : -INFINITY;
 }
 
 // A 32-bit buffer view of `bytes` bytes at `base`: loads past the end read 0
@@ -147,8 +175,9 @@ __device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t
 // Output row of (b, h): out = sum_j 2^(m_j - M) o_j / L over the row's run
 // partials.  The D columns are split into CG groups, one per workgroup of the
 // row.  Thread (rr, c) owns float4 column c of its group and the runs rr,
-// rr + R, ..., kMergeBatch at a time; the R thread sums are added in LDS in a
-// fixed order.  The first batch is requested before the row statistics.
+// rr + R, ..., kMergeBatch at a time; the R thread sums are added by a
+// butterfly inside each wavefront and then across wavefronts in a fixed
+// order.  The first batch is requested before the row statistics.
 constexpr int kMergeBatch = 4;
 
 template <int D, int CG>
@@ -165,14 +194,16 @@ struct MergeLoads {
       const int j = j0 + u * R;
       const int64_t i = run_index(p, r, j);
       v[u] = *reinterpret_cast<const float4*>(p.ws_o + i * D + col0 + 4 * c);
-      m[u] = j < r.nrun ? p.ws_rm[i] : -INFINITY;
+      m[u] = p.ws_rm[i];
     }
   }
 
-  __device__ __forceinline__ void add_to(float4& acc, float M) const {
+  // Runs j0 + u*R at or past nrun (re-reads of the last run) weigh 0.
+  __device__ __forceinline__ void add_to(float4& acc, float M, int j0, int nrun) const {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float w = m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[u] - M);
+      const bool live = j0 + u * R < nrun && m[u] != -INFINITY;
+      const float w = live ? __builtin_amdgcn_exp2f(m[u] - M) : 0.f;
       acc.x = fmaf(w, v[u].x, acc.x);
       acc.y = fmaf(w, v[u].y, acc.y);
       acc.z = fmaf(w, v[u].z, acc.z);
@@ -185,21 +216,31 @@ template <int D, bool BF, int CG>
 __device__ void merge_cols(const MergeParams& p, const Row& r, int bh, int col0,
                            const MergeLoads<D, CG>& first, float M, float L) {
   using ML = MergeLoads<D, CG>;
-  __shared__ float4 part[ML::R][ML::C4];
+  static_assert(ML::C4 <= kWave, "a wavefront holds every column of its group");
+  constexpr int NW = kMergeThreads / kWave;
+  __shared__ float4 part[NW][ML::C4];
   const int tid = threadIdx.x;
   const int c = tid % ML::C4, rr = tid / ML::C4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  first.add_to(acc, M);
+  first.add_to(acc, M, rr, r.nrun);
   for (int j0 = rr + ML::R * kMergeBatch; j0 < r.nrun; j0 += ML::R * kMergeBatch) {
     ML more;
     more.issue(p, r, j0, col0);
-    more.add_to(acc, M);
+    more.add_to(acc, M, j0, r.nrun);
   }
-  part[rr][c] = acc;
+  // Lanes c, c + C4, ... of a wavefront hold column c.
+#pragma unroll
+  for (int off = ML::C4; off < kWave; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off, kWave);
+    acc.y += __shfl_xor(acc.y, off, kWave);
+    acc.z += __shfl_xor(acc.z, off, kWave);
+    acc.w += __shfl_xor(acc.w, off, kWave);
+  }
+  if ((tid & (kWave - 1)) < ML::C4) part[tid / kWave][c] = acc;
   __syncthreads();
   if (rr == 0) {
     float4 t = part[0][c];
-    for (int i = 1; i < ML::R; ++i) {
+    for (int i = 1; i < NW; ++i) {
       t.x += part[i][c].x;
       t.y += part[i][c].y;
       t.z += part[i][c].z;
@@ -221,8 +262,7 @@ __device__ void merge_cols(const MergeParams& p, const Row& r, int bh, int col0,
 // kernel left its raw sum relative to the reference max of the run holding
 // that task, so its softmax weight is raw * 2^(m_run - lse / ln 2).  Pages
 // past the sequence get mass 0; for the group's first head the slice also
-// sets the page-max tails to -inf, and slice 0 writes the next query-summary
-// state of (b, g).
+// sets the page-max tails to -inf.
 struct PageLoads {
   float raw[kPagesPerThread], m[kPagesPerThread];
 
@@ -262,45 +302,83 @@ __device__ void finish_slice(const MergeParams& p, const Row& r, int bh, int sli
       buffer_store_f32(-INFINITY, pmax, pg >= r.npg ? pg * 4 : kDropOffset);
     }
   }
-  if (slice != 0 || (int)threadIdx.x >= 2 * D) return;
-  // Next summary state: group-mean query, heads added in head order.
-  const int which = (int)threadIdx.x >= D;
-  const int d = threadIdx.x - which * D;
-  const int64_t q0 = ((int64_t)r.b * p.Hq + (int64_t)r.g * p.G) * D + d;
-  float qv[kMaxGroup];
-#pragma unroll
-  for (int hq = 0; hq < kMaxGroup; ++hq) qv[hq] = q_value<BF>(f.q, q0 + (int64_t)min(hq, p.G - 1) * D);
-  const int64_t si = (((int64_t)which * p.B + r.b) * p.Hkv + r.g) * D + d;
-  const float sp = f.s_prev[si];
-  float acc = qv[0];
-#pragma unroll
-  for (int hq = 1; hq < kMaxGroup; ++hq)
-    if (hq < p.G) acc = __fadd_rn(acc, qv[hq]);
-  f.s_next[si] = ema_step(sp, __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
 }
+
+// Next query-summary state of (b, g), elements d and d + 1 of both
+// summaries: the group-mean query (heads added in head order, then scaled by
+// 1/G, the attention kernel's expression) and one EMA step of the fast and
+// the slow summary (GrowPage, Technical Details).  It needs only q and
+// s_prev; each query load brings both elements of a head.
+template <bool BF>
+struct SummaryStep {
+  uint32_t qb[kMaxGroup];   // bits of q[b, g*G + head, d .. d+1]
+  float sp[2][2];           // s_prev[which][b, g, d .. d+1]
+  int64_t si[2];            // index of (which, b, g, d)
+
+  __device__ __forceinline__ void issue(const MergeParams& p, int b, int g, int d, int D) {
+    const FinishParams& f = p.fin;
+    const int64_t q0 = ((int64_t)b * p.Hq + (int64_t)g * p.G) * D + d;
+#pragma unroll
+    for (int hq = 0; hq < kMaxGroup; ++hq)
+      qb[hq] = *reinterpret_cast<const uint32_t*>(f.q + q0 + (int64_t)min(hq, p.G - 1) * D);
+    si[0] = ((int64_t)b * p.Hkv + g) * D + d;
+    si[1] = si[0] + (int64_t)p.B * p.Hkv * D;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      sp[w][0] = f.s_prev[si[w]];
+      sp[w][1] = f.s_prev[si[w] + 1];
+    }
+  }
+
+  __device__ __forceinline__ void store(const MergeParams& p) const {
+    const FinishParams& f = p.fin;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float acc = bits_value<BF>((qb[0] >> (16 * e)) & 0xffffu);
+#pragma unroll
+      for (int hq = 1; hq < kMaxGroup; ++hq)
+        if (hq < p.G) acc = __fadd_rn(acc, bits_value<BF>((qb[hq] >> (16 * e)) & 0xffffu));
+      const float qbar = __fmul_rn(acc, f.inv_g);
+      f.s_next[si[0] + e] = ema_step(sp[0][e], qbar, f.alpha_fast);
+      f.s_next[si[1] + e] = ema_step(sp[1][e], qbar, f.alpha_slow);
+    }
+  }
+};
 
 // Each row has nsub = max(CG, nslice) workgroups: workgroup k merges column
 // group k (k < CG) and, with FINISH, finishes page slice k (k < nslice).
-// All of a workgroup's loads are requested before the row statistics are
-// reduced, so its data arrives in one memory round trip.
+// Once the row's metadata is in, every load of the workgroup goes out at
+// once and unconditionally (a workgroup with no column group or no slice
+// loads its neighbour's, which stay in cache), so the data arrives in one
+// memory round trip and the compiler's wait counts stay exact.
 template <int D, bool BF, bool FINISH, int CG>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p, int nslice,
                                                               int nsub) {
-  __shared__ float scratch[kMergeThreads / kWave];
+  __shared__ float scratch[2 * kMergeThreads / kWave];
   const int bh = blockIdx.x / nsub, sub = blockIdx.x % nsub;
   const Row r = row_of(p, bh, FINISH);
   const bool do_cols = sub < CG;
   const bool do_pages = FINISH && sub < nslice;
-  const int col0 = sub * (D / CG);
+  const int col0 = min(sub, CG - 1) * (D / CG);
   MergeLoads<D, CG> ml;
+  ml.issue(p, r, threadIdx.x / MergeLoads<D, CG>::C4, col0);
   PageLoads pl;
-  if (do_cols) ml.issue(p, r, threadIdx.x / MergeLoads<D, CG>::C4, col0);
-  if (do_pages) pl.issue(p, r, bh, sub);
+  if constexpr (FINISH) pl.issue(p, r, bh, min(sub, nslice - 1));
+  StatLoads st;
+  st.issue(p, r);
   float M, L;
-  const float lse_nat = row_lse(p, r, scratch, &L, &M);
+  const float lse_nat = row_lse(p, r, st, scratch, &L, &M);
   if (do_cols) merge_cols<D, BF, CG>(p, r, bh, col0, ml, M, L);
   if (sub == 0 && threadIdx.x == 0) p.lse[bh] = lse_nat;
   if (do_pages) finish_slice<BF>(p, r, bh, sub, D, pl, lse_nat);
+  // The group's first head, first workgroup, also steps the summaries.  (The
+  // same loads requested at kernel start measured slower in every merge
+  // kernel: they delay that workgroup's metadata round trip.)
+  if (FINISH && sub == 0 && r.hh == 0 && (int)threadIdx.x < D / 2) {
+    SummaryStep<BF> ss;
+    ss.issue(p, r.b, r.g, 2 * threadIdx.x, D);
+    ss.store(p);
+  }
 }
 
 // ---- Many rows: one wavefront per (row, page slice) ----------------------
@@ -343,10 +421,13 @@ __global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergePa
       const float* src = p.ws_o + i * D + CPL * lane;
 #pragma unroll
       for (int x = 0; x < CPL; ++x) ov[u][x] = src[x];
-      om[u] = j0 + u < r.nrun ? p.ws_rm[i] : -INFINITY;
+      om[u] = p.ws_rm[i];
     }
   };
-  if (do_out) issue_runs(0);
+  // Every load goes out unconditionally (slices past 0 load the partials
+  // too, and missing runs re-read the last one), so all arrive in one round
+  // trip and the compiler's wait counts stay exact.
+  issue_runs(0);
   // Raw page sums of the slice and the run maxima they are relative to.
   float raw[kWavePagesPerLane], rmx[kWavePagesPerLane];
   if constexpr (FINISH) {
@@ -362,15 +443,13 @@ __global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergePa
     }
   }
   // Row statistics over all runs, lanes strided over the runs.
-  float tm = -INFINITY, tl = 0.f;
-  for (int j = lane; j < max(r.nrun, 1); j += kWave) {
+  const int64_t i0 = run_index(p, r, lane);
+  const float m0 = p.ws_rm[i0], l0 = p.ws_rl[i0];
+  float tm = lane < r.nrun ? m0 : -INFINITY;
+  float tl = lane < r.nrun ? l0 : 0.f;
+  for (int j = lane + kWave; j < r.nrun; j += kWave) {
     const int64_t i = run_index(p, r, j);
-    const float m = j < r.nrun ? p.ws_rm[i] : -INFINITY;
-    const float l = p.ws_rl[i];
-    const float nm = fmaxf(tm, m);
-    tl = (tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - nm)) +
-         (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - nm));
-    tm = nm;
+    ml_combine(tm, tl, p.ws_rm[i], p.ws_rl[i]);
   }
   const float M = wave_max(tm);
   const float L = wave_sum(tm == -INFINITY ? 0.f : tl * __builtin_amdgcn_exp2f(tm - M));
@@ -383,7 +462,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergePa
     for (int j0 = 0;;) {
 #pragma unroll
       for (int u = 0; u < kWaveRunBatch; ++u) {
-        const float w = om[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(om[u] - M);
+        const bool live = j0 + u < r.nrun && om[u] != -INFINITY;
+        const float w = live ? __builtin_amdgcn_exp2f(om[u] - M) : 0.f;
 #pragma unroll
         for (int x = 0; x < CPL; ++x) acc[x] = fmaf(w, ov[u][x], acc[x]);
       }
@@ -417,24 +497,12 @@ __global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergePa
         buffer_store_f32(-INFINITY, pmax, pg >= r.npg ? pg * 4 : kDropOffset);
       }
     }
-    if (slice != 0) return;
-    // Next summary state of (b, g): 2*D elements over the 64 lanes.
-#pragma unroll
-    for (int e = 0; e < 2 * CPL; ++e) {
-      const int x = e * kWave + lane;
-      const int which = x >= D;
-      const int d = x - which * D;
-      const int64_t q0 = ((int64_t)r.b * p.Hq + (int64_t)r.g * p.G) * D + d;
-      float qv[kMaxGroup];
-#pragma unroll
-      for (int hq = 0; hq < kMaxGroup; ++hq) qv[hq] = q_value<BF>(f.q, q0 + (int64_t)min(hq, p.G - 1) * D);
-      const int64_t si = (((int64_t)which * p.B + r.b) * p.Hkv + r.g) * D + d;
-      const float sp = f.s_prev[si];
-      float acc = qv[0];
-#pragma unroll
-      for (int hq = 1; hq < kMaxGroup; ++hq)
-        if (hq < p.G) acc = __fadd_rn(acc, qv[hq]);
-      f.s_next[si] = ema_step(sp, __fmul_rn(acc, f.inv_g), which ? f.alpha_slow : f.alpha_fast);
+    // The group's first head, slice 0, also steps the summaries (elements
+    // 2*lane and 2*lane + 1).
+    if (slice == 0 && 2 * lane < D) {
+      SummaryStep<BF> ss;
+      ss.issue(p, r.b, r.g, 2 * lane, D);
+      ss.store(p);
     }
   }
 }
@@ -448,6 +516,11 @@ __global__ void __launch_bounds__(kMergeThreads) finish_kernel(const MergeParams
   PageLoads pl;
   pl.issue(p, r, bh, slice);
   finish_slice<BF>(p, r, bh, slice, D, pl, p.lse[bh]);
+  if (slice == 0 && r.hh == 0 && (int)threadIdx.x < D / 2) {
+    SummaryStep<BF> ss;
+    ss.issue(p, r.b, r.g, 2 * threadIdx.x, D);
+    ss.store(p);
+  }
 }
 
 static MergeParams merge_params(const kvpage_shape& s, const int32_t* group_offsets,
