@@ -61,7 +61,8 @@ def measured_traffic(config: str):
     return None
 
 
-def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = True):
+def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = True,
+                stream_kv=None):
     """Time workload `name`: one kvpage_decode_step call per step.
 
     Two timed regions of `steps` steps each, both with the cache flush before
@@ -71,21 +72,27 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
       * roofline: the split-attention kernel's own dispatch records its start
         and end (hipExtLaunchKernelGGL events) -> that kernel's duration.
     They are separate because kernel-level timestamps add a few microseconds
-    to a step.
+    to a step.  stream_kv (KVPAGE_FLAG_STREAM_KV) defaults to "the tables
+    share no page".
     """
     import torch
 
     from paged_kv_cache_07_amd import binding, workloads as W
     from paged_kv_cache_07_amd.device import DecodeStep
 
+    # Tables that share no page take the streaming tile loads
+    # (KVPAGE_FLAG_STREAM_KV); the prefix-sharing batch keeps cached loads.
     if isinstance(name, tuple):      # ("custom", contexts, split)
         _, ctx, split = name
         wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21)
-        ds = DecodeStep(wl, budget=budget, split_tokens=split)
+        split_tokens = split
         name = f"{len(ctx)}x{ctx[0]}/S{split}"
     else:
         wl = W.make(name)
-        ds = DecodeStep(wl, budget=budget)
+        split_tokens = None
+    if stream_kv is None:
+        stream_kv = not wl.shares_pages()
+    ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens, stream_kv=stream_kv)
     kv = W.kv_bytes(wl)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -126,7 +133,7 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
         "workload": name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
         "page_size": wl.page_size, "split_tokens": wl.split_tokens, "dtype": wl.dtype,
         "ctx_total": int(wl.ctx_lens.sum()), "n_tasks": n_tasks, "kv_bytes": kv,
-        "kv_bytes_unique": W.kv_bytes(wl, unique=True),
+        "kv_bytes_unique": W.kv_bytes(wl, unique=True), "stream_kv": stream_kv,
         "step_ms_mean": float(step_ms.mean()), "step_ms_p50": float(np.median(step_ms)),
         "step_ms_p10": float(np.percentile(step_ms, 10)), "step_ms_p90": float(np.percentile(step_ms, 90)),
         "attn_ms_mean": float(attn_ms.mean()), "attn_ms_p50": float(np.median(attn_ms)),
@@ -210,11 +217,14 @@ def main():
             "step_ms_mean": r["step_ms_mean"], "attn_ms_mean": r["attn_ms_mean"],
             "kv_bytes": r["kv_bytes"], "kv_bytes_unique": r["kv_bytes_unique"],
             "n_tasks": r["n_tasks"], "B": r["B"], "Hq": r["Hq"], "Hkv": r["Hkv"],
-            "dtype": r["dtype"], "steps": k,
+            "dtype": r["dtype"], "stream_kv": r["stream_kv"], "steps": k,
         }
 
     # The split policy (kvpage_choose_split) on short batches, where the
     # fixed 256-token split leaves wavefronts idle, beside the fixed split.
+    # Both with cached tile loads: streaming loads slow a step that leaves
+    # wavefronts idle (the fixed split here) by ~6%, which would flatter the
+    # policy.
     policy = {}
     if args.policy:
         from paged_kv_cache_07_amd import binding as K
@@ -225,8 +235,8 @@ def main():
                                  wl.num_pages, wl.dtype, wl.scale)
             split = K.kvpage_choose_split(shape, wl.ctx_lens.tolist())
             k = max(10, args.steps // 4)
-            fixed = time_config(("custom", ctx, 256), k, 3, flush)
-            chosen = time_config(("custom", ctx, split), k, 3, flush)
+            fixed = time_config(("custom", ctx, 256), k, 3, flush, stream_kv=False)
+            chosen = time_config(("custom", ctx, split), k, 3, flush, stream_kv=False)
             policy[f"{len(ctx)}x{ctx[0]}"] = {
                 "split_chosen": split, "step_ms_split256": fixed["step_ms_mean"],
                 "step_ms_chosen": chosen["step_ms_mean"],
@@ -251,14 +261,16 @@ def main():
         "data": "synthetic: seeded N(0,1) fp16 q/K/V, pages scattered by a seeded permutation",
         "config": {"workload": "B1 long-context paged GQA decode step", "B": 1, "context": 32768,
                    "Hq": 32, "Hkv": 8, "d": 128, "page_size": 16, "split_tokens": 256,
-                   "pool_pages": 4096, "budgeting_outputs": True, "cold_cache": flush},
+                   "pool_pages": 4096, "budgeting_outputs": True, "cold_cache": flush,
+                   "stream_kv": head["stream_kv"]},
         "steps_per_s": 1e3 / head["step_ms_mean"],
         "frac_hbm_peak_step": kv / head["step_ms_mean"] / 1e6 / HBM_PEAK_GBS,
         "step_ms_p50": head["step_ms_p50"], "step_ms_p10": head["step_ms_p10"],
         "step_ms_p90": head["step_ms_p90"], "n_tasks": head["n_tasks"], "kv_bytes": kv,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kvpage::split_attn_kernel<128, f16, budget, fused queue>",
+                     "kernel": "kvpage::split_attn_kernel<128, f16, budget, fused queue"
+                               + (", streaming loads>" if head["stream_kv"] else ">"),
                      "attn_ms_mean": head["attn_ms_mean"],
                      "algorithmic_bytes_per_launch": kv},
         "also": also,

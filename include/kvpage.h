@@ -88,9 +88,23 @@ typedef struct {
   int32_t seq, kv_head, tok_begin, tok_end;
 } kvpage_task;
 
+/* Shape flags.
+ *   KVPAGE_FLAG_STREAM_KV  the caller promises that no K/V page is referenced
+ *       by more than one sequence in the call (no prefix sharing).  The
+ *       attention kernel then marks its K/V tile loads non-temporal so they
+ *       stream past the caches.  It changes no result, only speed: 2-7%
+ *       faster when the step has at least about one task per wavefront of
+ *       the GPU (Hkv * sum_b ceil(ctx_b / split_tokens) >= 4 per compute
+ *       unit, which kvpage_choose_split aims for), ~6% slower on shorter
+ *       steps.  Leave it clear when block tables share pages: shared pages
+ *       are then served from cache (15% faster on a batch of 64 sequences
+ *       sharing 128 prefix pages than with the flag set). */
+#define KVPAGE_FLAG_STREAM_KV 1u
+
 /* Problem shape.  Supported by the kernels: page_size == 16; d in {64, 128};
  * 1 <= Hq / Hkv <= 8; split_tokens a multiple of page_size in [16, 256];
- * dtype f16 or bf16; scale finite and > 0.  flags must be 0. */
+ * dtype f16 or bf16; scale finite and > 0.  flags: 0 or
+ * KVPAGE_FLAG_STREAM_KV (any other bit is KVPAGE_ERR_INVALID_ARG). */
 typedef struct {
   int32_t B, Hq, Hkv, d, page_size, split_tokens, max_pages, num_pages;
   int32_t dtype; /* kvpage_dtype */

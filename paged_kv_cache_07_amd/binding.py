@@ -116,6 +116,11 @@ def _stream(stream):
     return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
 
 
+# kvpage_shape.flags: no K/V page is referenced by two sequences in the call;
+# the attention kernel's tile loads are then non-temporal.
+KVPAGE_FLAG_STREAM_KV = 1
+
+
 def make_shape(B, Hq, Hkv, d, page_size, split_tokens, max_pages, num_pages, dtype, scale,
                flags=0) -> kvpage_shape:
     code = {"f16": KVPAGE_F16, "bf16": KVPAGE_BF16}.get(dtype, dtype)

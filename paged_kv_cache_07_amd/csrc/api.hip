@@ -40,7 +40,7 @@ int check_shape(const kvpage_shape* s) {
   if (s->split_tokens % s->page_size != 0) return KVPAGE_ERR_INVALID_ARG;
   if (!(s->scale > 0.0f) || !isfinite(s->scale)) return KVPAGE_ERR_INVALID_ARG;
   if (s->dtype != KVPAGE_F16 && s->dtype != KVPAGE_BF16) return KVPAGE_ERR_INVALID_ARG;
-  if (s->flags != 0) return KVPAGE_ERR_INVALID_ARG;
+  if ((s->flags & ~KVPAGE_FLAG_STREAM_KV) != 0) return KVPAGE_ERR_INVALID_ARG;
   // Token indices (including one split past the end) must fit in int32.
   if ((int64_t)s->max_pages * s->page_size + s->split_tokens > INT32_MAX)
     return KVPAGE_ERR_INVALID_ARG;

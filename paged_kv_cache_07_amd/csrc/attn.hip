@@ -155,6 +155,15 @@ __device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, bool hi_ha
 // sequence b's split count and the inclusive prefix of task counts, so the
 // (sequence, KV head, split) of queue position t is one ballot away.  This is
 // the same enumeration as the queue-build kernel.
+// One tile load.  With STREAM the access is marked non-temporal, so the lines
+// stream past the caches instead of displacing what is reused (page ids,
+// query rows, partials).  Only right when no page is read twice in a call.
+template <bool STREAM, typename V>
+__device__ __forceinline__ V tile_load(const char* addr) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const V*>(addr));
+  else return *reinterpret_cast<const V*>(addr);
+}
+
 struct SeqScan {
   int ctx, ns, cnt, incl, total;
 };
@@ -176,7 +185,7 @@ __device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, 
   return q;
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const AttnParams p) {
   using E = Elem<BF>;
@@ -347,7 +356,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       const char* base = kpool + off;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(base + koff[kb]);
+        const u32x4 w = tile_load<STREAM, u32x4>(base + koff[kb]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) dst[4 * kb + x] = w[x];
       }
@@ -356,11 +365,11 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (VW == 4) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(base + voff[e]);
+          const u32x4 w = tile_load<STREAM, u32x4>(base + voff[e]);
 #pragma unroll
           for (int x = 0; x < 4; ++x) dst[VW * e + x] = w[x];
         } else {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(base + voff[e]);
+          const u32x2 w = tile_load<STREAM, u32x2>(base + voff[e]);
 #pragma unroll
           for (int x = 0; x < VW; ++x) dst[VW * e + x] = w[x];
         }
@@ -557,7 +566,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         const char* base = (has_next ? kpool : vpool) + tile_offset(pid, has_next ? nxt.g : g, p.Hkv, D) * 2;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(base + koff[kb]);
+          const u32x4 w = tile_load<STREAM, u32x4>(base + koff[kb]);
 #pragma unroll
           for (int x = 0; x < 4; ++x) buf[slot][4 * kb + x] = w[x];
         }
@@ -660,10 +669,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   }
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
-  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT>;
+  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, STREAM>;
   // Resident workgroups of this instance per device, found once.  Concurrent
   // first calls may both look it up; they store the same value.
   static std::atomic<int> resident_wg[64];
@@ -706,35 +715,35 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
 #define KVPAGE_ATTN_DEPTH 2
 #endif
 
-template <bool FUSEDQ, int PPT>
+template <bool FUSEDQ, int PPT, bool STREAM>
 static hipError_t dispatch_ppt(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                                int max_wg) {
   constexpr int DP = KVPAGE_ATTN_DEPTH < PPT ? KVPAGE_ATTN_DEPTH : PPT;
   const bool bf = s.dtype == KVPAGE_BF16;
   if (s.d == 128) {
-    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                       : launch_one<128, true, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
-    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
-               : launch_one<128, false, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                       : launch_one<128, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+               : launch_one<128, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
   }
-  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                     : launch_one<64, true, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
-  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg)
-             : launch_one<64, false, false, DP, FUSEDQ, PPT>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                     : launch_one<64, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+             : launch_one<64, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
 }
 
 // The instance with the fewest pages per task that holds one split: a task
 // issues loads for all of its instance's pages, so a short split run by the
 // 16-page instance would spend most of its loads on repeats.
-template <bool FUSEDQ>
+template <bool FUSEDQ, bool STREAM>
 static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                            int max_wg) {
   const int pages = s.split_tokens / kPage;
-  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return dispatch_ppt<FUSEDQ, 16>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return dispatch_ppt<FUSEDQ, 16, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 // Wavefronts of one resident round per compute unit (one workgroup per CU).
@@ -784,9 +793,13 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.c2 = s.scale * 1.4426950408889634f;
   p.inv_g = 1.0f / (float)G;
   const bool fused = tasks_out != nullptr;
+  const bool bud = budget != nullptr;
+  const bool stream_kv = (s.flags & KVPAGE_FLAG_STREAM_KV) != 0;
   if (fused)
-    return dispatch<true>(s, p, capacity, budget != nullptr, stream, ev_start, ev_stop, max_wg);
-  return dispatch<false>(s, p, capacity, budget != nullptr, stream, ev_start, ev_stop, max_wg);
+    return stream_kv ? dispatch<true, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+              : dispatch<true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return stream_kv ? dispatch<false, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+            : dispatch<false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 }  // namespace kvpage

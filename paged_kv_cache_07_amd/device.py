@@ -40,13 +40,16 @@ class DecodeStep:
     flips them for the next step.
     """
 
-    def __init__(self, wl, device="cuda", budget=True, split_tokens=None):
+    def __init__(self, wl, device="cuda", budget=True, split_tokens=None, stream_kv=False):
         torch = _torch()
         self.wl = wl
         self.device = torch.device(device)
         self.split_tokens = split_tokens or wl.split_tokens
+        # stream_kv: the caller's promise that no page is shared between
+        # sequences (KVPAGE_FLAG_STREAM_KV); it changes no result.
         self.shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, self.split_tokens,
-                                  wl.max_pages, wl.num_pages, wl.dtype, wl.scale)
+                                  wl.max_pages, wl.num_pages, wl.dtype, wl.scale,
+                                  K.KVPAGE_FLAG_STREAM_KV if stream_kv else 0)
         self.capacity = K.kvpage_queue_capacity(self.shape)
         ws = K.kvpage_workspace_bytes(self.shape, self.capacity)
         dev = self.device

@@ -112,6 +112,11 @@ class Workload:
         ids = [self.block_tables[b, : self.pages_of(b)] for b in range(self.B)]
         return np.unique(np.concatenate(ids)) if ids else np.zeros(0, np.int32)
 
+    def shares_pages(self) -> bool:
+        """True if some physical page is in the used part of two sequences' tables."""
+        n = sum(self.pages_of(b) for b in range(self.B))
+        return len(self.referenced_pages()) < n
+
 
 def kv_bytes(wl: Workload, unique: bool = False) -> int:
     """Algorithmic K+V bytes one decode step must read.

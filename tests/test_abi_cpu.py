@@ -45,6 +45,14 @@ def test_capacity_and_workspace_arithmetic():
     assert K.kvpage_workspace_bytes(s, cap) == (64 + cap * 4 * (128 + 2)) * 4
 
 
+def test_stream_flag_is_accepted():
+    """KVPAGE_FLAG_STREAM_KV changes no size: same capacity and workspace."""
+    s, plain = _shape(flags=K.KVPAGE_FLAG_STREAM_KV), _shape()
+    cap = K.kvpage_queue_capacity(s)
+    assert cap == K.kvpage_queue_capacity(plain) > 0
+    assert K.kvpage_workspace_bytes(s, cap) == K.kvpage_workspace_bytes(plain, cap) > 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(Hq=30), K.KVPAGE_ERR_INVALID_ARG),          # Hq % Hkv != 0
     (dict(split_tokens=40), K.KVPAGE_ERR_INVALID_ARG),  # split not a page multiple
@@ -54,7 +62,8 @@ def test_capacity_and_workspace_arithmetic():
     (dict(max_pages=0), K.KVPAGE_ERR_INVALID_ARG),
     (dict(B=-1), K.KVPAGE_ERR_INVALID_ARG),
     (dict(max_pages=(1 << 27)), K.KVPAGE_ERR_INVALID_ARG),  # tokens overflow int32
-    (dict(flags=1), K.KVPAGE_ERR_INVALID_ARG),
+    (dict(flags=2), K.KVPAGE_ERR_INVALID_ARG),          # only KVPAGE_FLAG_STREAM_KV is defined
+    (dict(flags=K.KVPAGE_FLAG_STREAM_KV | 4), K.KVPAGE_ERR_INVALID_ARG),
 ])
 def test_invalid_shapes_are_rejected(kw, status):
     s = _shape(**kw)

@@ -27,13 +27,14 @@ def _need_gpu():
     binding.lib()
 
 
-def _run(wl, budget=True, split_tokens=None, label="", one_call=False):
+def _run(wl, budget=True, split_tokens=None, label="", one_call=False, stream_kv=False):
     """Separate calls (queue, attention + merge, page-mass finish), or with
     one_call the single kvpage_decode_step call bench.py times."""
     from paged_kv_cache_07_amd.device import DecodeStep
     say("run", label or wl.name, "ctx", wl.ctx_lens.tolist()[:8], "G", wl.G, "d", wl.d,
-        wl.dtype, "split", split_tokens or wl.split_tokens, "budget", budget, "one_call", one_call)
-    ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens)
+        wl.dtype, "split", split_tokens or wl.split_tokens, "budget", budget, "one_call", one_call,
+        "stream_kv", stream_kv)
+    ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens, stream_kv=stream_kv)
     if one_call:
         ds.step()
     else:
@@ -152,9 +153,10 @@ def test_oracle_sized_configs_all_outputs(name, div):
                                   "b4_bimodal"])
 def test_full_size_sampled_rows(name):
     """Full-size workloads in the launch configuration bench.py times (one
-    kvpage_decode_step call), sampled rows against the oracle."""
+    kvpage_decode_step call, streaming tile loads unless pages are shared),
+    sampled rows against the oracle."""
     wl = W.make(name)
-    _, res = _run(wl, label=f"{name}-full", one_call=True)
+    _, res = _run(wl, label=f"{name}-full", one_call=True, stream_kv=not wl.shares_pages())
     tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
     assert res["n_tasks"] == n
     assert np.array_equal(res["tasks"], tasks) and np.array_equal(res["group_offsets"], offs)
@@ -422,3 +424,26 @@ def test_bad_caller_data_stays_in_its_rows(path):
         assert_close("mass", res["mass"][b], ref["mass"][b])
         assert_close("page_max", res["page_max"][:, b], ref["page_max"][:, b])
     assert_close("s_next", res["s_next"], ref["s_next"])
+
+
+@pytest.mark.parametrize("case", ["tiny", "edge", "b8_bimodal_small", "b64_prefix_small"])
+@pytest.mark.parametrize("one_call", [True, False])
+def test_stream_kv_changes_no_bits(case, one_call):
+    """KVPAGE_FLAG_STREAM_KV only marks the tile loads non-temporal: every
+    output is bit-identical to the cached loads (and matches the oracle)."""
+    if case == "tiny":
+        wl = W.make("tiny")
+    elif case == "edge":
+        wl = W.custom([0, 1, 15, 16, 17, 255, 256, 257, 1000], Hq=8, Hkv=2, d=64, dtype="bf16", seed=31)
+    elif case == "b8_bimodal_small":
+        wl = W.make("b8_bimodal", ctx_divisor=32)
+    else:
+        wl = W.make("b64_prefix", ctx_divisor=16)
+    outs = []
+    for stream_kv in (False, True):
+        _, res = _run(wl, label=f"{case}-stream{int(stream_kv)}", one_call=one_call, stream_kv=stream_kv)
+        outs.append(res)
+    a, b = outs
+    for key in ("tasks", "group_offsets", "out_bits", "lse", "mass", "page_max", "s_next"):
+        assert np.array_equal(a[key], b[key]), key
+    compare_step(b, oracle_step(wl), label=case)
