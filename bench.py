@@ -141,6 +141,48 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
     }
 
 
+def time_append(name: str, calls: int, flush: bool):
+    """kvpage_append_kv on workload `name`: one token per sequence per call,
+    pages taken from the pool's unreferenced pages; HIP events around each
+    call, caches flushed before it.  The lengths grow by one per call (a
+    sequence whose table row is full is left as it is and flagged in
+    `status`, as the call defines)."""
+    import torch
+
+    from paged_kv_cache_07_amd import binding, workloads as W
+    from paged_kv_cache_07_amd.device import DecodeStep, host_to_device
+
+    wl = W.make(name)
+    ds = DecodeStep(wl, budget=False)
+    used = np.zeros(wl.num_pages, dtype=bool)
+    used[wl.referenced_pages()] = True
+    ds.set_free_list(np.flatnonzero(~used).astype(np.int32))
+    rng = np.random.default_rng(7)
+    rows = (wl.B, wl.Hkv, wl.d)
+    x = rng.standard_normal(rows).astype(np.float32)
+    k_new = host_to_device(W.f32_to_bf16_bits(x) if wl.dtype == "bf16" else x.astype(np.float16),
+                           wl.dtype, ds.device)
+    v_new = k_new.clone()
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(calls + 3)]
+    for a, b in ev:       # the first three calls are warm-up
+        if flush:
+            torch.sum(flush_buf, dim=0, out=sink[0])
+        a.record()
+        binding.kvpage_append_kv(ds.shape, k_new, v_new, ds.k_pool, ds.v_pool, ds.block_tables,
+                                 ds.ctx_lens, ds.ctx_next, ds.free_pages, ds.free_count,
+                                 ds.free_count_next, ds.append_status)
+        b.record()
+        ds.ctx_lens, ds.ctx_next = ds.ctx_next, ds.ctx_lens
+        ds.free_count, ds.free_count_next = ds.free_count_next, ds.free_count
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_ms(b) for a, b in ev[3:]]) * 1e3
+    return {"calls": calls, "us_mean": float(us.mean()), "us_p50": float(np.median(us)),
+            "bytes_written": wl.B * wl.Hkv * wl.d * 2 * 2,
+            "status": int(ds.append_status.item()), "B": wl.B}
+
+
 def cpu_baseline(seconds: float = 12.0):
     """The fp64 oracle on the host: full B1 steps repeated for ~``seconds``."""
     from threadpoolctl import threadpool_limits
@@ -175,6 +217,8 @@ def main():
                     help="comma-separated extra workloads reported beside the headline one")
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the KV append (one token per sequence) on B8 and B64")
     ap.add_argument("--policy", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the split policy on short batches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -243,6 +287,11 @@ def main():
                 "speedup": fixed["step_ms_mean"] / chosen["step_ms_mean"],
                 "kv_gbs_step_chosen": chosen["kv_bytes"] / chosen["step_ms_mean"] / 1e6}
 
+    append = {}
+    if args.append:
+        for name in ("b8_bimodal", "b64_prefix"):
+            append[name] = time_append(name, 40, flush)
+
     kv = head["kv_bytes"]
     achieved = kv / head["attn_ms_mean"] / 1e6
     traffic = measured_traffic(args.config)
@@ -277,6 +326,8 @@ def main():
     }
     if policy:
         result["split_policy"] = policy
+    if append:
+        result["kv_append"] = append
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result))
