@@ -1,7 +1,8 @@
 // Log-sum-exp merge of split partials, and the page-mass / summary finish.
 //
-// The split partials of one (sequence, query head) are combined in split
-// order: with M = max_j m_j and w_j = 2^(m_j - M), out = sum_j w_j o_j /
+// The run partials of one (sequence, query head) are combined in a fixed
+// order (per-thread sums, then butterflies, so the bits do not depend on
+// timing): with M = max_j m_j and w_j = 2^(m_j - M), out = sum_j w_j o_j /
 // sum_j w_j l_j and lse = ln 2 * (M + log2 sum_j w_j l_j).  Page mass is the
 // softmax weight of each logical page (GrowPage, Abstract: page-level KV
 // budgeting), finished here from the per-task page sums that the attention
