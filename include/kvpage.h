@@ -75,7 +75,7 @@ extern "C" {
 typedef enum {
   KVPAGE_OK = 0,
   KVPAGE_ERR_INVALID_ARG = -1, /* null pointer, inconsistent or out-of-range shape */
-  KVPAGE_ERR_UNSUPPORTED = -2, /* valid shape this build has no kernel for        */
+  KVPAGE_ERR_UNSUPPORTED = -2, /* valid shape the library has no kernel for       */
   KVPAGE_ERR_CAPACITY = -3,    /* task capacity below kvpage_queue_capacity()     */
   KVPAGE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed       */
 } kvpage_status;
