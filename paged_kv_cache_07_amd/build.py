@@ -19,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvpage.so")
+C_ABI_CHECK = os.path.join(ROOT, "tests", "cabi", "kvpage_c_abi_check")
 SOURCES = ("api.hip", "queue.hip", "attn.hip", "merge.hip", "append.hip")
 ARCH = "gfx950"
 
@@ -62,6 +63,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
     link_out = _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    # The standalone C ABI check (plain host code linked against the library,
+    # no Python), run by the GPU tests.
+    check_src = os.path.join(ROOT, "tests", "cabi", "c_abi_check.cpp")
+    if os.path.exists(check_src):
+        link_out += _run([cc, "-O2", "-std=c++17", "-I", INCLUDE, check_src, "-o", C_ABI_CHECK,
+                          "-L", HERE, "-lkvpage", "-Wl,-rpath,$ORIGIN/../../paged_kv_cache_07_amd"])
     if verbose:
         for _, out in results:
             if out.strip():
