@@ -42,7 +42,11 @@
  * Struct arguments (kvpage_shape, kvpage_budget) are HOST pointers read
  * during the call; every other pointer is a DEVICE pointer.  Calls enqueue
  * work on `stream` and return without synchronizing; the library never
- * allocates, frees or synchronizes and keeps no per-call state.
+ * allocates, frees or synchronizes and keeps no per-call state (only a
+ * per-device count of resident workgroups, found on first use).  Calls that
+ * may run at the same time (other streams) need their own queue, workspace
+ * and output buffers; inputs may be shared.  Every call can be captured in
+ * a HIP graph: it enqueues kernels only (no memset, copy or allocation).
  *
  * Alignment: q, k_pool, v_pool and the workspace must be 16-byte aligned,
  * out 8-byte aligned (vector loads and stores); anything else is
