@@ -82,11 +82,16 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
 
     # Tables that share no page take the streaming tile loads
     # (KVPAGE_FLAG_STREAM_KV); the prefix-sharing batch keeps cached loads.
-    if isinstance(name, tuple):      # ("custom", contexts, split)
+    if isinstance(name, tuple) and name[0] == "custom":     # ("custom", contexts, split)
         _, ctx, split = name
         wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21)
         split_tokens = split
         name = f"{len(ctx)}x{ctx[0]}/S{split}"
+    elif isinstance(name, tuple):                            # ("named", workload, split)
+        _, base, split = name
+        wl = W.make(base)
+        split_tokens = split
+        name = f"{base}/S{split}"
     else:
         wl = W.make(name)
         split_tokens = None
@@ -279,26 +284,35 @@ def main():
             "dtype": r["dtype"], "stream_kv": r["stream_kv"], "steps": k,
         }
 
-    # The split policy (kvpage_choose_split) on short batches, where the
-    # fixed 256-token split leaves wavefronts idle, beside the fixed split.
-    # Both with cached tile loads: streaming loads slow a step that leaves
-    # wavefronts idle (the fixed split here) by ~6%, which would flatter the
-    # policy.
+    # The split policy (kvpage_choose_split) beside the fixed 256-token split,
+    # both in the same load mode: three short batches, where the fixed split
+    # leaves wavefronts idle, with cached tile loads (streaming loads slow
+    # such a step by ~6%, which would flatter the policy); and the B8 bimodal
+    # lengths with streaming loads, where 256-token tasks end in a partial
+    # round.
     policy = {}
     if args.policy:
         from paged_kv_cache_07_amd import binding as K
         from paged_kv_cache_07_amd import workloads as W
-        for ctx in ([8192], [4096] * 4, [16384]):
-            wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21, fill_pools=False)
+        cases = [(("custom", ctx), f"{len(ctx)}x{ctx[0]}", False)
+                 for ctx in ([8192], [4096] * 4, [16384])]
+        cases.append((("named", "b8_bimodal"), "b8_bimodal", True))
+        for spec, label, stream_kv in cases:
+            if spec[0] == "custom":
+                wl = W.custom(spec[1], Hq=32, Hkv=8, d=128, seed=21, fill_pools=False)
+            else:
+                wl = W.make(spec[1], fill_pools=False)
             shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, 256, wl.max_pages,
-                                 wl.num_pages, wl.dtype, wl.scale)
+                                 wl.num_pages, wl.dtype, wl.scale,
+                                 K.KVPAGE_FLAG_STREAM_KV if stream_kv else 0)
             split = K.kvpage_choose_split(shape, wl.ctx_lens.tolist())
             k = max(10, args.steps // 4)
-            fixed = time_config(("custom", ctx, 256), k, 3, flush, stream_kv=False)
-            chosen = time_config(("custom", ctx, split), k, 3, flush, stream_kv=False)
-            policy[f"{len(ctx)}x{ctx[0]}"] = {
-                "split_chosen": split, "step_ms_split256": fixed["step_ms_mean"],
-                "step_ms_chosen": chosen["step_ms_mean"],
+            fixed = time_config((*spec, 256), k, 3, flush, stream_kv=stream_kv)
+            chosen = time_config((*spec, split), k, 3, flush, stream_kv=stream_kv)
+            policy[label] = {
+                "split_chosen": split, "stream_kv": stream_kv,
+                "step_ms_split256": fixed["step_ms_mean"], "step_ms_chosen": chosen["step_ms_mean"],
+                "attn_ms_split256": fixed["attn_ms_mean"], "attn_ms_chosen": chosen["attn_ms_mean"],
                 "speedup": fixed["step_ms_mean"] / chosen["step_ms_mean"],
                 "kv_gbs_step_chosen": chosen["kv_bytes"] / chosen["step_ms_mean"] / 1e6}
 

@@ -226,17 +226,24 @@ int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_
 
 /* Split size for one decode step, chosen per workload (PersistentKV
  * summary, Summary: its throughput gains come from a policy that picks the
- * decode configuration for each workload).  Returns the longest split in
- * {256, 128, 64, 32, 16} tokens whose queue still holds at least one task
- * per resident wavefront of the attention kernel, i.e.
- * Hkv * sum_b ceil(ctx_b / S) >= wavefronts; the page size (16) if none does;
- * 256 if every context is empty.  Longer splits need fewer partials and
- * merge work, but a queue shorter than the resident wavefronts leaves the
- * GPU partly idle; the kernel instance for short splits issues loads for
- * only the pages a split can hold.  On MI355X this choice was the fastest
- * (or within 2% of it) for every workload measured.
+ * decode configuration for each workload).  Among the splits S in
+ * {256, 128, 64, 32, 16} tokens whose queue holds at least one task per
+ * resident wavefront of the attention kernel (n = Hkv * sum_b ceil(ctx_b / S)
+ * >= wavefronts), returns the one whose busiest wavefront has the least work
+ * under the kernel's schedule: with rounds = ceil(n / (16 * wavefronts)) and
+ * c = ceil(n / (rounds * wavefronts)) tasks per chunk, c * rounds tasks of
+ * S / 16 pages each plus a fixed cost per task (measured: half a page with
+ * KVPAGE_FLAG_STREAM_KV in shape.flags, one and a half without); ties go to
+ * the longer split.  The page size (16) if no split fills the wavefronts,
+ * 256 if every context is empty.  A queue shorter than the resident
+ * wavefronts leaves the GPU partly idle; one that ends in a partial round
+ * leaves a tail (6656 tasks of 256 tokens on 1024 wavefronts: 7 per
+ * wavefront where 6.5 would do; with streaming loads split 128 gives 13 per
+ * wavefront and ran 3.5% faster).  The kernel instance for short splits
+ * issues loads for only the pages a split can hold.
  *   shape: B, Hq, Hkv, d, page_size, max_pages, num_pages, dtype, scale and
- *     flags as for the other calls; split_tokens is ignored.
+ *     flags as for the other calls (flags as the step will use them);
+ *     split_tokens is ignored.
  *   ctx_lens_host: HOST array of B context lengths, each in [0, max_pages *
  *     page_size].
  *   wavefronts: resident wavefronts to fill; <= 0 queries the current device

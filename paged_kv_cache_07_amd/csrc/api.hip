@@ -20,6 +20,7 @@ hipError_t launch_append(const kvpage_shape&, const void*, const void*, void*, v
                          const int32_t*, int32_t*, const int32_t*, const int32_t*, int32_t*,
                          int32_t*, hipStream_t);
 int split_attn_waves_per_cu();
+int split_attn_chunk_max();
 hipError_t launch_merge(const kvpage_shape&, const int32_t*, int32_t, const void*, void*, float*,
                         hipStream_t);
 hipError_t launch_merge_finish(const kvpage_shape&, const kvpage_budget&, const void*,
@@ -282,12 +283,31 @@ int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
   }
   const int32_t longest = 16 * t.page_size;
   if (total == 0) return longest;
-  for (int32_t split = longest; split > t.page_size; split /= 2) {
+  // Among the splits whose queue holds a task for every resident wavefront,
+  // the one whose busiest wavefront has the least work under the attention
+  // kernel's schedule (rounds of chunks of at most chunk_max positions):
+  // its tasks times (pages per task + a task's fixed cost), the fixed cost
+  // measured at half a page with streaming tile loads and one and a half
+  // with cached ones.  Ties go to the longer split; none qualifies: the page
+  // size.
+  const int64_t chunk_max = split_attn_chunk_max();
+  const int64_t task_cost2 = (t.flags & KVPAGE_FLAG_STREAM_KV) ? 1 : 3;   // twice the fixed cost
+  int32_t best = 0;
+  int64_t best_cost = INT64_MAX;
+  for (int32_t split = longest; split >= t.page_size; split /= 2) {
     int64_t tasks = 0;
     for (int b = 0; b < t.B; ++b) tasks += (ctx_lens_host[b] + split - 1) / split;
-    if (tasks * t.Hkv >= waves) return split;
+    tasks *= t.Hkv;
+    if (tasks < waves) continue;
+    const int64_t rounds = (tasks + waves * chunk_max - 1) / (waves * chunk_max);
+    const int64_t c = (tasks + waves * rounds - 1) / (waves * rounds);
+    const int64_t cost = c * rounds * (2 * (split / t.page_size) + task_cost2);   // twice the work
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = split;
+    }
   }
-  return t.page_size;
+  return best ? best : t.page_size;
 }
 
 const char* kvpage_status_string(int status) {

@@ -749,6 +749,9 @@ static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capac
 // Wavefronts of one resident round per compute unit (one workgroup per CU).
 int split_attn_waves_per_cu() { return kWavesPerGroup; }
 
+// Most queue positions in one chunk of the schedule.
+int split_attn_chunk_max() { return kRunMax; }
+
 // Fused queue build: B <= 64 sequences (one lane each in the task lookup).
 bool split_attn_can_fuse_queue(const kvpage_shape& s) { return s.B >= 1 && s.B <= kWave; }
 

@@ -149,14 +149,16 @@ def test_oracle_sized_configs_all_outputs(name, div):
     compare_step(res, oracle_step(wl), label=name)
 
 
-@pytest.mark.parametrize("name", ["b1", "b8_bimodal", "b8_uniform", "b8_zipf", "b64_prefix",
-                                  "b4_bimodal"])
-def test_full_size_sampled_rows(name):
-    """Full-size workloads in the launch configuration bench.py times (one
-    kvpage_decode_step call, streaming tile loads unless pages are shared),
-    sampled rows against the oracle."""
-    wl = W.make(name)
-    _, res = _run(wl, label=f"{name}-full", one_call=True, stream_kv=not wl.shares_pages())
+@pytest.mark.parametrize("name,split", [("b1", 256), ("b8_bimodal", 256), ("b8_uniform", 256),
+                                        ("b8_zipf", 256), ("b64_prefix", 256), ("b4_bimodal", 256),
+                                        ("b8_bimodal", 128)])
+def test_full_size_sampled_rows(name, split):
+    """Full-size workloads in the launch configurations bench.py times (one
+    kvpage_decode_step call, streaming tile loads unless pages are shared;
+    B8 bimodal also at the split the policy picks for it), sampled rows
+    against the oracle."""
+    wl = dataclasses.replace(W.make(name), split_tokens=split)
+    _, res = _run(wl, label=f"{name}-full-S{split}", one_call=True, stream_kv=not wl.shares_pages())
     tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
     assert res["n_tasks"] == n
     assert np.array_equal(res["tasks"], tasks) and np.array_equal(res["group_offsets"], offs)
