@@ -171,7 +171,11 @@ struct SeqScan {
 __device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, int Hkv, int S,
                                                 int max_pages, int lane) {
   SeqScan q;
-  q.ctx = lane < B ? clamp_ctx(ctx_lens[lane], max_pages) : 0;
+  // Unconditional load (B >= 1 here), masked after: lanes past B count 0.
+  // Under a branch the load came after two more rounds of kernel-argument
+  // loads; this way it leaves after the first (B1: 0.3 us earlier).
+  const int32_t raw = ctx_lens[min(lane, B - 1)] & -(int32_t)(lane < B);
+  q.ctx = clamp_ctx(raw, max_pages);
   q.ns = (q.ctx + S - 1) / S;
   q.cnt = q.ns * Hkv;
   int v = q.cnt;
