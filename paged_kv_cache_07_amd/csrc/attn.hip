@@ -178,12 +178,17 @@ __device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, 
   q.ctx = clamp_ctx(raw, max_pages);
   q.ns = (q.ctx + S - 1) / S;
   q.cnt = q.ns * Hkv;
+  // Inclusive prefix over the lanes: within each row of 16 lanes by DPP row
+  // shifts (a lane with no source reads 0), then the row totals added in.
   int v = q.cnt;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  v += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
   q.incl = v;
   q.total = __builtin_amdgcn_readlane(v, kWave - 1);
   return q;
