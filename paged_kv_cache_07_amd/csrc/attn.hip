@@ -21,7 +21,8 @@
 //   * P V comes from 16x16x16 MFMAs whose P operand is the score tile's own
 //     register layout, so no lane shuffles are needed between the two
 //     contractions;
-//   * K and V tiles stream through a ring of DEPTH register buffers.
+//   * K and V tiles stream through a ring of DEPTH register buffers, with
+//     non-temporal loads (STREAM) when the caller says no page is shared.
 //
 // Outputs per run go to the workspace at the run's first queue position:
 // m (log2 domain), l = sum exp2(y - m) and the unnormalised o = sum
