@@ -22,7 +22,11 @@
 //     register layout, so no lane shuffles are needed between the two
 //     contractions;
 //   * K and V tiles stream through a ring of DEPTH register buffers, with
-//     non-temporal loads (STREAM) when the caller says no page is shared.
+//     non-temporal loads (STREAM) when the caller says no page is shared;
+//   * with one sequence (SPEC), each wavefront requests its first task's page
+//     ids, query rows and first tiles before the length has arrived, on the
+//     guess that the context fills the table row, and keeps them when the
+//     lengths confirm it.
 //
 // Outputs per run go to the workspace at the run's first queue position:
 // m (log2 domain), l = sum exp2(y - m) and the unnormalised o = sum
@@ -30,6 +34,7 @@
 #include <float.h>
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include <hip/hip_ext.h>
@@ -88,27 +93,37 @@ struct Elem<true> {  // bfloat16
 };
 
 struct AttnParams {
+  // What a wavefront needs first, kept together so that one batch of
+  // kernel-argument loads brings it: lengths, page ids, query and summary
+  // rows and the first tiles.
+  const int32_t* ctx_lens;
+  const int32_t* block_tables;
   const uint16_t* q;
   const uint16_t* k_pool;
   const uint16_t* v_pool;
-  const int32_t* block_tables;
+  const float* s_prev;
+  int32_t split_tokens, B, Hq, Hkv, G, max_pages, num_pages, capacity;
+  int32_t nwaves;   // wavefronts in the grid
+  // Predicting instance (fused build, one sequence): the chunk length and
+  // split count the schedule has when the context fills the table row, and
+  // 1 / spec_ns rounded to float.
+  int32_t spec_c, spec_ns;
+  float spec_rcp;
+  // Division by split_tokens and by the number of wavefronts in the grid.
+  DivMagic div_split, div_waves;
   const kvpage_task* tasks;
   const int32_t* n_tasks;
-  // Fused queue build (one-call step): lengths in, queue arrays out.
-  const int32_t* ctx_lens;
+  // Fused queue build (one-call step): queue arrays out.
   kvpage_task* tasks_out;
   int32_t* group_offsets_out;
   int32_t* n_tasks_out;
-  int32_t split_tokens;
   int32_t* ws_hdr;
   float* ws_o;
   float* ws_rm;
   float* ws_rl;
   float* page_mass;
-  const float* s_prev;
   float* page_max;
   float alpha_fast, alpha_slow;
-  int32_t B, Hq, Hkv, G, max_pages, num_pages, capacity;
   float scale, c2, inv_g;
 };
 
@@ -167,17 +182,23 @@ __device__ __forceinline__ V tile_load(const char* addr) {
 
 struct SeqScan {
   int ctx, ns, cnt, incl, total;
+  float rns;   // 1 / ns (approximate)
 };
 
-__device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, int Hkv, int S,
-                                                int max_pages, int lane) {
+// Lane b's length (lanes past B repeat the last one; the scan masks them).
+// The load is unconditional (B >= 1 here): under a branch it came after two
+// more rounds of kernel-argument loads; this way it leaves after the first
+// (0.3 us earlier).
+__device__ __forceinline__ int32_t load_length(const int32_t* ctx_lens, int B, int lane) {
+  return ctx_lens[min(lane, B - 1)];
+}
+
+__device__ __forceinline__ SeqScan scan_lengths(int32_t raw, int B, int Hkv, int S,
+                                                DivMagic div_s, int max_pages, int lane) {
   SeqScan q;
-  // Unconditional load (B >= 1 here), masked after: lanes past B count 0.
-  // Under a branch the load came after two more rounds of kernel-argument
-  // loads; this way it leaves after the first (B1: 0.3 us earlier).
-  const int32_t raw = ctx_lens[min(lane, B - 1)] & -(int32_t)(lane < B);
-  q.ctx = clamp_ctx(raw, max_pages);
-  q.ns = (q.ctx + S - 1) / S;
+  q.ctx = clamp_ctx(raw & -(int32_t)(lane < B), max_pages);
+  q.ns = (int)div_by((uint32_t)(q.ctx + S - 1), div_s);
+  q.rns = __builtin_amdgcn_rcpf((float)q.ns);
   q.cnt = q.ns * Hkv;
   // Inclusive prefix over the lanes: within each row of 16 lanes by DPP row
   // shifts (a lane with no source reads 0), then the row totals added in.
@@ -195,9 +216,10 @@ __device__ __forceinline__ SeqScan scan_lengths(const int32_t* ctx_lens, int B, 
   return q;
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM, bool SPEC>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const AttnParams p) {
+  static_assert(FUSEDQ || !SPEC, "the first-task prediction belongs to the fused queue build");
   using E = Elem<BF>;
   constexpr int KB = D / 32;   // 16x16x32 MFMAs per page for the scores
   constexpr int VD = D / 16;   // output column blocks; V halves per lane per token
@@ -220,6 +242,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   constexpr int kOpRows = 16;
   constexpr int kQStage = kOpRows * D / 2 + 2 * D;
   constexpr int DPL = D / kWave;                  // summary elements per lane
+  constexpr int kMaxG = 8;                        // query heads per KV head, at most
 
   // Per-wave LDS: staged query / summary rows, and the scores of the task.
   __shared__ uint32_t lds_q[kWavesPerGroup * kQStage];
@@ -237,38 +260,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   const int n = lane & 15;       // column inside the row
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * kWavesPerGroup + wave;
-  const int nwaves = gridDim.x * kWavesPerGroup;
-  int ntask;
-  SeqScan sq;
-  if constexpr (FUSEDQ) {
-    sq = scan_lengths(p.ctx_lens, p.B, p.Hkv, p.split_tokens, p.max_pages, lane);
-    ntask = min(sq.total, p.capacity);
-    if (blockIdx.x == 0 && wave == 0) {
-      if (lane < p.B) {
-        const int start = sq.incl - sq.cnt;
-        for (int g = 0; g < p.Hkv; ++g)
-          p.group_offsets_out[lane * p.Hkv + g] = min(start + g * sq.ns, p.capacity);
-      }
-      if (lane == 0) {
-        p.group_offsets_out[p.B * p.Hkv] = ntask;
-        p.n_tasks_out[0] = ntask;
-      }
-    }
-  } else {
-    ntask = min(p.n_tasks[0], p.capacity);
-  }
-  // The queue is cut into chunks of c consecutive positions (c <= kRunMax,
-  // sized so every wavefront gets nearly the same number of chunks); wave gw
-  // runs chunks gw, gw + nwaves, ...  Run partials start at multiples of c.
-  const int rounds = max(1, (ntask + nwaves * kRunMax - 1) / (nwaves * kRunMax));
-  const int c = max(1, (ntask + nwaves * rounds - 1) / (nwaves * rounds));
-  const int nchunks = (ntask + c - 1) / c;
-  if (blockIdx.x == 0 && wave == 0 && lane == 0) p.ws_hdr[0] = c;
-  int chunk = gw;
-  if (chunk >= nchunks) return;
-  int chunk_end = min((chunk + 1) * c, ntask);   // exclusive
-  const int t_first = chunk * c;
-
+  const int nwaves = p.nwaves;   // gridDim would add the 256-byte hidden argument block
   const int G = p.G;
   const bool is_head = n < G;
   const bool is_lead = BUDGET && (n == G || n == G + NPC);
@@ -287,6 +279,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   struct Task {
     int t, b, g, tok_begin, tok_end, ntok, npg, lp0;
   };
+  SeqScan sq = {0, 0, 0, 0, 0};
   // Queue entry t: read from the queue, or (fused build) derived from the lengths.
   auto fetch = [&](int t) {
     kvpage_task tk;
@@ -297,7 +290,12 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       const int ns = __builtin_amdgcn_readlane(sq.ns, bq);
       const int ctx = __builtin_amdgcn_readlane(sq.ctx, bq);
       const int k = t - start;
-      const int gq = k / ns;
+      // k / ns from the float reciprocal: the quotient is below Hkv, so the
+      // estimate is off by at most one; corrected both ways.
+      const float rns = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sq.rns), bq));
+      int gq = (int)((float)k * rns);
+      gq -= (uint32_t)gq * (uint32_t)ns > (uint32_t)k ? 1 : 0;
+      gq += (uint32_t)(gq + 1) * (uint32_t)ns <= (uint32_t)k ? 1 : 0;
       const int j = k - gq * ns;
       tk.seq = bq;
       tk.kv_head = gq;
@@ -404,23 +402,55 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     __builtin_amdgcn_wave_barrier();
     if constexpr (BUDGET) {
       const float* sp = reinterpret_cast<const float*>(qs + kOpRows * D / 2);
+      // Every read first, so that they share one LDS round trip: this lane's
+      // elements of the first kMaxG staged rows (rows from G on are read and
+      // not used) and of both summaries.
+      float hv[kMaxG][DPL];
+      float sv[2][DPL];
+#pragma unroll
+      for (int h = 0; h < kMaxG; ++h) {
+        if constexpr (DPL == 2) {
+          const uint32_t w = qs[h * D / 2 + lane];
+          hv[h][0] = E::value(w & 0xffffu);
+          hv[h][1] = E::value(w >> 16);
+        } else {
+#pragma unroll
+          for (int x = 0; x < DPL; ++x) hv[h][x] = E::value(qh[h * D + DPL * lane + x]);
+        }
+      }
+#pragma unroll
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) sv[which][x] = sp[which * D + DPL * lane + x];
+      uint32_t pcs[2][NPC][DPL];
 #pragma unroll
       for (int x = 0; x < DPL; ++x) {
-        const int d = DPL * lane + x;
-        float acc = E::value(qh[d]);
-        for (int h = 1; h < G; ++h) acc = __fadd_rn(acc, E::value(qh[h * D + d]));
+        float acc = hv[0][x];
+#pragma unroll
+        for (int h = 1; h < kMaxG; ++h)
+          if (h < G) acc = __fadd_rn(acc, hv[h][x]);
         const float qbar = __fmul_rn(acc, p.inv_g);
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
-          float rem = ema_step(sp[which * D + d], qbar, which ? p.alpha_slow : p.alpha_fast);
+          float rem = ema_step(sv[which][x], qbar, which ? p.alpha_slow : p.alpha_fast);
 #pragma unroll
           for (int piece = 0; piece < NPC; ++piece) {
-            const uint32_t pc = E::bits(rem);
-            qh[(G + which * NPC + piece) * D + d] = (uint16_t)pc;
-            rem = __fsub_rn(rem, E::value(pc));
+            pcs[which][piece][x] = E::bits(rem);
+            rem = __fsub_rn(rem, E::value(pcs[which][piece][x]));
           }
         }
       }
+#pragma unroll
+      for (int which = 0; which < 2; ++which)
+#pragma unroll
+        for (int piece = 0; piece < NPC; ++piece) {
+          const int row = G + which * NPC + piece;
+          if constexpr (DPL == 2)
+            qs[row * D / 2 + lane] = pcs[which][piece][0] | (pcs[which][piece][1] << 16);
+          else
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) qh[row * D + DPL * lane + x] = (uint16_t)pcs[which][piece][x];
+        }
       __builtin_amdgcn_wave_barrier();
     }
     const bool has_row = n < G + (BUDGET ? 2 * NPC : 0);
@@ -433,16 +463,97 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     __builtin_amdgcn_wave_barrier();
   };
 
-  Task cur = fetch(t_first);
-  // Query rows first: they arrive with the page ids, so the operand is built
-  // while the first tiles are in flight.
-  Rows rows = load_rows(cur);
-  int32_t ids = load_page_ids(cur);
   uint32_t buf[DEPTH][TW];
-#pragma unroll
-  for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
   u32x4 qop[KB];
-  build_operand(rows, qop);
+  int ntask;
+  // Fused build with one sequence (SPEC): the first task of this wavefront
+  // when the context fills the table row.  Its page ids, query rows and first
+  // tiles are requested right behind the length and its operand is built
+  // before the lengths are scanned; all of it is kept if the lengths give
+  // that task.  This saves the dependent round trip from length to page ids.
+  Task spec = {0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t ids_spec = 0;
+  if constexpr (FUSEDQ) {
+    int32_t raw_len;
+    if constexpr (SPEC) {
+      const int pps = p.split_tokens / kPage;
+      const int ts = gw * p.spec_c;
+      // ts / spec_ns through the float reciprocal (off by at most one for
+      // operands below 2^22), corrected both ways.
+      int gs = (int)((float)ts * p.spec_rcp);
+      gs -= gs * p.spec_ns > ts ? 1 : 0;
+      gs += (gs + 1) * p.spec_ns <= ts ? 1 : 0;
+      spec.b = 0;
+      spec.g = min(max(gs, 0), p.Hkv - 1);
+      spec.lp0 = min((ts - spec.g * p.spec_ns) * pps, p.max_pages - 1);
+      spec.npg = min(pps, p.max_pages - spec.lp0);
+      // The length first, then page ids and rows; the tiles wait for the
+      // page ids (and so for the length issued before them), the operand for
+      // the rows.  Measured against page ids first: 0.2 us faster at one
+      // 32K sequence, the same within noise elsewhere.
+      raw_len = load_length(p.ctx_lens, p.B, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      ids_spec = p.block_tables[min(spec.lp0 + lane, p.max_pages - 1)];
+      const Rows rows_spec = load_rows(spec);
+      __builtin_amdgcn_sched_barrier(0);   // all three leave before the wait for the page ids
+#pragma unroll
+      for (int tau = 0; tau < DEPTH; ++tau) load_tile(spec, ids_spec, tau, buf[tau]);
+      // Keep the first use of the length below these loads: hoisted above a
+      // tile, it made that tile wait for the length.
+      __builtin_amdgcn_sched_barrier(0);
+      build_operand(rows_spec, qop);
+    } else {
+      raw_len = load_length(p.ctx_lens, p.B, lane);
+    }
+    sq = scan_lengths(raw_len, p.B, p.Hkv, p.split_tokens, p.div_split, p.max_pages, lane);
+    ntask = min(sq.total, p.capacity);
+    if (blockIdx.x == 0 && wave == 0) {
+      if (lane < p.B) {
+        const int start = sq.incl - sq.cnt;
+        for (int g = 0; g < p.Hkv; ++g)
+          p.group_offsets_out[lane * p.Hkv + g] = min(start + g * sq.ns, p.capacity);
+      }
+      if (lane == 0) {
+        p.group_offsets_out[p.B * p.Hkv] = ntask;
+        p.n_tasks_out[0] = ntask;
+      }
+    }
+  } else {
+    ntask = min(p.n_tasks[0], p.capacity);
+  }
+  // The queue is cut into chunks of c consecutive positions (c <= kRunMax,
+  // sized so every wavefront gets nearly the same number of chunks); wave gw
+  // runs chunks gw, gw + nwaves, ...  Run partials start at multiples of c.
+  int c;
+  if (ntask <= nwaves * kRunMax) {   // one round
+    c = max(1, (int)div_by((uint32_t)(ntask + nwaves - 1), p.div_waves));
+  } else {
+    const int rounds = (ntask + nwaves * kRunMax - 1) / (nwaves * kRunMax);
+    c = (ntask + nwaves * rounds - 1) / (nwaves * rounds);
+  }
+  if (blockIdx.x == 0 && wave == 0 && lane == 0) p.ws_hdr[0] = c;
+  int chunk = gw;
+  if (chunk * c >= ntask) return;   // chunk past the last one
+  int chunk_end = min((chunk + 1) * c, ntask);   // exclusive
+  const int t_first = chunk * c;
+
+  Task cur = fetch(t_first);
+  int32_t ids;
+  bool predicted = false;
+  if constexpr (SPEC) predicted = cur.b == 0 && cur.g == spec.g && cur.lp0 == spec.lp0;
+  if (predicted) {
+    // Same rows and page ids as requested above; tiles past the task's last
+    // page differ from what the loads below would give but are never read.
+    ids = lane < cur.npg ? ids_spec : 0;
+  } else {
+    // Query rows first: they arrive with the page ids, so the operand is
+    // built while the first tiles are in flight.
+    const Rows rows = load_rows(cur);
+    ids = load_page_ids(cur);
+#pragma unroll
+    for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
+    build_operand(rows, qop);
+  }
 
   // Run state: the running partial of consecutive tasks of one (b, g).
   int run_start = t_first;
@@ -521,7 +632,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 
     // ---- the next task of this wave (or this one again at the end) ----
     const bool in_chunk = cur.t + 1 < chunk_end;
-    const bool next_chunk = !in_chunk && chunk + nwaves < nchunks;
+    const bool next_chunk = !in_chunk && (chunk + nwaves) * c < ntask;
     const bool has_next = in_chunk || next_chunk;
     const int tn = in_chunk ? cur.t + 1 : (next_chunk ? (chunk + nwaves) * c : cur.t);
     const Task nxt = fetch(tn);
@@ -626,18 +737,23 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         if (lane < nk) p.tasks_out[run_start + lane] = lds_task[wave][lane];
       }
       if (BUDGET && kin == 0) {
-        // A run of one task: its reference is the run's, so the page values
-        // in registers are final (page 4r + u of head / summary column n).
+        // A run of one task: its reference is the run's, so the staged page
+        // values are final.  Lane (h, pg) = (lane / 16, lane % 16) stores page
+        // pg of head h (of summary h for the page maxima): one store per four
+        // heads instead of one per page and column.
+        __builtin_amdgcn_wave_barrier();
+        const int pg = lane & 15;
+        const int hl = lane >> 4;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int pg = 4 * r + u;
-          if (pg < npg) {
-            if (is_head)
-              p.page_mass[((int64_t)b * p.Hq + (int64_t)g * G + n) * p.max_pages + run_lp0 + pg] = keep[u];
-            if (is_lead)
-              p.page_max[(((int64_t)(n == G ? 0 : 1) * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0 + pg] = keep[u];
-          }
+        for (int hb = 0; hb < kMaxG; hb += 4) {
+          const int h = hb + hl;
+          if (hb < G && h < G && pg < npg)
+            p.page_mass[((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0 + pg] =
+                lds_mass[wave][0][h][pg];
         }
+        if (hl < 2 && pg < npg)
+          p.page_max[(((int64_t)hl * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0 + pg] =
+              lds_pmax[wave][0][hl][pg];
       } else if constexpr (BUDGET) {
         // Raw page sums move to the run's final reference, the one its
         // partial carries; pages of a run are consecutive in the sequence.
@@ -679,10 +795,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   }
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM, bool SPEC>
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
-  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, STREAM>;
+  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, STREAM, SPEC>;
   // Resident workgroups of this instance per device, found once.  Concurrent
   // first calls may both look it up; they store the same value.
   static std::atomic<int> resident_wg[64];
@@ -707,12 +823,28 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
   if (max_wg > 0 && grid64 > max_wg) grid64 = max_wg;
   const int grid = (int)grid64;
   if (grid <= 0) return hipSuccess;
+  AttnParams a = p;
+  a.nwaves = grid * kWavesPerGroup;
+  a.div_waves = div_magic((uint32_t)grid * kWavesPerGroup);
+  a.spec_c = 0;
+  a.spec_ns = 1;
+  a.spec_rcp = 1.0f;
+  if (SPEC) {
+    // The schedule the kernel derives from a length of max_pages * P.
+    const int64_t ns = ((int64_t)p.max_pages * kPage + p.split_tokens - 1) / p.split_tokens;
+    const int64_t ntask = std::min<int64_t>(ns * p.Hkv, capacity);
+    const int64_t nw = (int64_t)grid * kWavesPerGroup;
+    const int64_t rounds = std::max<int64_t>(1, (ntask + nw * kRunMax - 1) / (nw * kRunMax));
+    a.spec_c = (int32_t)std::max<int64_t>(1, (ntask + nw * rounds - 1) / (nw * rounds));
+    a.spec_ns = (int32_t)ns;
+    a.spec_rcp = 1.0f / (float)ns;
+  }
   if (ev_start || ev_stop) {
     // Timestamps taken by the dispatch itself: start and end of this kernel.
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, ev_start,
-                          ev_stop, 0, p);
+                          ev_stop, 0, a);
   } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -725,35 +857,35 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
 #define KVPAGE_ATTN_DEPTH 2
 #endif
 
-template <bool FUSEDQ, int PPT, bool STREAM>
+template <bool FUSEDQ, int PPT, bool STREAM, bool SPEC>
 static hipError_t dispatch_ppt(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                                int max_wg) {
   constexpr int DP = KVPAGE_ATTN_DEPTH < PPT ? KVPAGE_ATTN_DEPTH : PPT;
   const bool bf = s.dtype == KVPAGE_BF16;
   if (s.d == 128) {
-    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                       : launch_one<128, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
-    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-               : launch_one<128, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                       : launch_one<128, true, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
+               : launch_one<128, false, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
   }
-  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                     : launch_one<64, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
-  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-             : launch_one<64, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                     : launch_one<64, true, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
+             : launch_one<64, false, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
 }
 
 // The instance with the fewest pages per task that holds one split: a task
 // issues loads for all of its instance's pages, so a short split run by the
 // 16-page instance would spend most of its loads on repeats.
-template <bool FUSEDQ, bool STREAM>
+template <bool FUSEDQ, bool STREAM, bool SPEC>
 static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                            int max_wg) {
   const int pages = s.split_tokens / kPage;
-  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return dispatch_ppt<FUSEDQ, 16, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, STREAM, SPEC>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, STREAM, SPEC>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return dispatch_ppt<FUSEDQ, 16, STREAM, SPEC>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 // Wavefronts of one resident round per compute unit (one workgroup per CU).
@@ -805,14 +937,24 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.scale = s.scale;
   p.c2 = s.scale * 1.4426950408889634f;
   p.inv_g = 1.0f / (float)G;
+  p.nwaves = 0;
+  p.spec_c = 0;
+  p.spec_ns = 1;
+  p.spec_rcp = 1.0f;
+  p.div_split = div_magic((uint32_t)s.split_tokens);
+  p.div_waves = div_magic(1);
   const bool fused = tasks_out != nullptr;
   const bool bud = budget != nullptr;
   const bool stream_kv = (s.flags & KVPAGE_FLAG_STREAM_KV) != 0;
+  // One sequence: the instance that predicts each wavefront's first task.
+  if (fused && s.B == 1)
+    return stream_kv ? dispatch<true, true, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+              : dispatch<true, false, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
   if (fused)
-    return stream_kv ? dispatch<true, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-              : dispatch<true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return stream_kv ? dispatch<false, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-            : dispatch<false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+    return stream_kv ? dispatch<true, true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+              : dispatch<true, false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return stream_kv ? dispatch<false, true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+            : dispatch<false, false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 }  // namespace kvpage

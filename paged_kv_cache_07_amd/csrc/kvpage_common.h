@@ -39,6 +39,31 @@ __device__ __forceinline__ int32_t clamp_page(int32_t page, int32_t num_pages) {
   return min(max(page, 0), num_pages - 1);
 }
 
+// Unsigned division by a divisor fixed for a launch, as a multiply-high and
+// two shifts (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, section 4, the round-up method for 32-bit
+// words): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+// t = mulhi(m, n) gives n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0)
+// for every 32-bit n.
+struct DivMagic {
+  uint32_t m, s1, s2;
+};
+
+inline DivMagic div_magic(uint32_t d) {   // d >= 1
+  uint32_t l = 0;
+  while (((uint64_t)1 << l) < d) ++l;
+  DivMagic r;
+  r.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+  r.s1 = l < 1 ? l : 1;
+  r.s2 = l > 1 ? l - 1 : 0;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t div_by(uint32_t n, DivMagic dm) {
+  const uint32_t t = __umulhi(dm.m, n);
+  return (t + ((n - t) >> dm.s1)) >> dm.s2;
+}
+
 // Group-mean query component: heads summed in head order, then scaled by
 // 1/G.  Used by the attention kernel (summary dot products) and by the
 // page-mass kernel (s_next), so both see identical bits.

@@ -323,6 +323,42 @@ def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
                          label=f"{wl.name} wg{max_wg} S{split}")
 
 
+@pytest.mark.parametrize("ctx,extra_pages,split,max_wg", [
+    (32768, 0, 256, 0),    # context fills the table row: every first task as predicted
+    (32768, 0, 256, 3),    # the same with long wavefront runs (chunks of 15 tasks)
+    (4000, 6, 256, 0),     # same split count as a full row: predicted, last split shorter
+    (4000, 40, 256, 0),    # table wider by more than a split: predictions fail
+    (1, 0, 256, 0), (17, 3, 64, 0), (257, 0, 128, 0), (5000, 0, 16, 0), (3000, 1, 32, 2)])
+def test_one_sequence_first_task_prediction(ctx, extra_pages, split, max_wg):
+    """One sequence in the one-call step: each wavefront requests its first
+    task's page ids, query rows and first tiles on the guess that the context
+    fills the table row, and keeps them only if the lengths give that task.
+    Whether the guess holds, holds with a shorter last split or fails, the
+    bits equal the separate calls (which never guess) and match the oracle."""
+    from paged_kv_cache_07_amd import binding
+    from paged_kv_cache_07_amd.device import DecodeStep
+    max_pages = -(-ctx // 16) + extra_pages
+    wl = W.custom([ctx], Hq=32, Hkv=8, d=128, seed=40 + ctx % 97, max_pages=max_pages)
+    wl.s_prev = np.random.default_rng(9).standard_normal(wl.s_prev.shape).astype(np.float32)
+    ref = oracle_step(wl, split_tokens=split)
+    for budget, stream_kv in ((True, True), (False, False)):
+        say("predict", ctx, "table", max_pages, "split", split, "max_wg", max_wg,
+            "budget", budget, "stream", stream_kv)
+        a = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
+        a.run()
+        ra = a.results()
+        b = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
+        b.step(opts=binding.make_opts(max_workgroups=max_wg) if max_wg else None)
+        rb = b.results()
+        keys = ["out_bits", "lse", "tasks", "group_offsets"] + (
+            ["mass", "page_max", "s_next"] if budget else [])
+        # A different grid folds tasks into different runs: then the values
+        # agree to rounding only, the queue still bit for bit.
+        for key in keys if not max_wg else ["tasks", "group_offsets"]:
+            assert np.array_equal(ra[key], rb[key]), key
+        compare_step(rb, ref, budget=budget, label=f"ctx{ctx} table{max_pages} S{split}")
+
+
 @pytest.mark.parametrize("ctx", [[8192], [4096] * 4, [100, 3000, 0, 700], [32768]])
 def test_chosen_split_all_outputs(ctx):
     """The split the policy picks for this device (short splits for short
