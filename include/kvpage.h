@@ -63,7 +63,9 @@
  * split_tokens tokens inside the table row, task counts to `capacity`.  A
  * violation therefore gives wrong values for the rows it touches and never
  * an access outside the buffers described here.  (kvpage_append_kv checks
- * its page ids and lengths and reports them in its status word.)
+ * its page ids and lengths and reports them in its status word.)  A caller
+ * who wants the violations reported runs kvpage_check_inputs, a separate
+ * read-only pass that writes them to a device status word (debug checks).
  */
 #ifndef KVPAGE_H
 #define KVPAGE_H
@@ -252,6 +254,40 @@ int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_
  * if the device query fails).  Enqueues nothing. */
 int32_t kvpage_choose_split(const kvpage_shape* shape, const int32_t* ctx_lens_host,
                             int32_t wavefronts);
+
+/* Status bits kvpage_check_inputs writes to its device status word. */
+enum {
+  KVPAGE_CHECK_LENGTH = 1,   /* a length outside [0, max_pages * page_size] */
+  KVPAGE_CHECK_PAGE = 2,     /* a block-table entry a sequence uses outside [0, num_pages) */
+  KVPAGE_CHECK_QUEUE = 4     /* the queue differs from the one kvpage_build_queue writes */
+};
+
+/* Debug checks of the data-dependent preconditions that the other calls
+ * assume and do not report (they clamp instead; see Errors above).  A
+ * read-only pass, separate from the decode kernels, for a caller who wants
+ * violations reported:
+ *   KVPAGE_CHECK_LENGTH: some ctx_lens[b] outside [0, max_pages * page_size];
+ *   KVPAGE_CHECK_PAGE: some block_tables[b, p] with p * page_size < ctx_b
+ *     (ctx_b clamped into that range) outside [0, num_pages);
+ *   KVPAGE_CHECK_QUEUE (only when tasks, group_offsets and n_tasks are
+ *     given): *n_tasks, group_offsets or one of the first *n_tasks entries of
+ *     tasks differs from what kvpage_build_queue writes for the clamped
+ *     lengths, or *n_tasks lies outside [0, capacity].
+ *   ctx_lens: [B] int32; block_tables: [B, max_pages] int32; tasks:
+ *     [capacity] kvpage_task; group_offsets: [B * Hkv + 1] int32; n_tasks:
+ *     one int32; all device.  tasks, group_offsets and n_tasks are either
+ *     all NULL or all given; capacity is then checked as for
+ *     kvpage_build_queue.
+ *   status: one int32, device, written with the KVPAGE_CHECK_* bits found
+ *     (0 when every check passes).  The call enqueues two kernels (one clears
+ *     the word, one checks) and reads nothing else.
+ * shape: B, Hkv, page_size, split_tokens, max_pages and num_pages are used;
+ * the other fields are checked as for the other calls.  Negative
+ * kvpage_status on invalid arguments (nothing enqueued). */
+int kvpage_check_inputs(const kvpage_shape* shape, const int32_t* ctx_lens,
+                        const int32_t* block_tables, const kvpage_task* tasks,
+                        const int32_t* group_offsets, const int32_t* n_tasks, int32_t capacity,
+                        int32_t* status, hipStream_t stream);
 
 /* Status bits kvpage_append_kv writes to its device status word. */
 enum {

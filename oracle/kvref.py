@@ -28,6 +28,10 @@ What is computed, and where it comes from:
   article, Technical Details: a page is acquired at a capacity boundary;
   "Elastic KV Cache for LLM Serving", 2 Background and Motivation: the paged
   pool is fixed-size blocks handed out from an integer free list).
+* Input checks -- what the decode step assumes of its integer inputs, as
+  plain definitions: lengths within the table row, the table entries a
+  sequence uses inside the pool, and a queue equal to ``build_queue`` of the
+  lengths (each clamped into the row first).
 * Query summaries -- GrowPage (Abstract; aitrending.vip article, Technical
   Details) keeps dual-timescale query summaries.  Here: per (sequence, KV
   group) a fast and a slow exponential moving average of the group-mean query,
@@ -48,11 +52,16 @@ __all__ = [
     "widen", "build_queue", "gather_offsets", "logical_rows", "attention",
     "update_summaries", "summary_page_max", "decode_step", "append_kv",
     "APPEND_FULL", "APPEND_NO_PAGE", "APPEND_BAD_PAGE",
+    "check_inputs", "CHECK_LENGTH", "CHECK_PAGE", "CHECK_QUEUE",
 ]
 
 APPEND_FULL = 1      # status bit: a sequence had no room left in its block-table row
 APPEND_NO_PAGE = 2   # status bit: the free list ran out
 APPEND_BAD_PAGE = 4  # status bit: a page id outside the pool (free list or table)
+
+CHECK_LENGTH = 1     # status bit: a length outside [0, max_pages * P]
+CHECK_PAGE = 2       # status bit: a table entry a sequence uses outside the pool
+CHECK_QUEUE = 4      # status bit: the queue is not build_queue of the (clamped) lengths
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -277,3 +286,40 @@ def append_kv(k_pool, v_pool, block_tables, ctx_lens, k_new, v_new, free_pages, 
         v_pool[page, :, t % page_size, :] = v_new[b]
         ctx[b] = t + 1
     return k_pool, v_pool, bt, ctx, free_count - taken, status
+
+
+def check_inputs(ctx_lens, block_tables, num_pages: int, page_size: int, Hkv: int,
+                 split_tokens: int, capacity=None, tasks=None, group_offsets=None, n_tasks=None):
+    """Status bits for the integer inputs of a decode step (see the header).
+
+    * ``CHECK_LENGTH``: some length outside ``[0, max_pages * P]``.
+    * ``CHECK_PAGE``: for some sequence ``b`` and page ``p`` with
+      ``p * P < ctx_b`` (``ctx_b`` clamped into ``[0, max_pages * P]``), the
+      table entry ``block_tables[b, p]`` is outside ``[0, num_pages)``.
+    * ``CHECK_QUEUE`` (only when a queue is given): ``n_tasks`` is outside
+      ``[0, capacity]``, or ``n_tasks``, ``group_offsets`` or the first
+      ``n_tasks`` rows of ``tasks`` differ from ``build_queue`` of the
+      clamped lengths.
+    """
+    bt = np.asarray(block_tables, dtype=np.int64)
+    max_pages = bt.shape[1]
+    status = 0
+    ctx = [int(c) for c in ctx_lens]
+    clamped = []
+    for c in ctx:
+        if c < 0 or c > max_pages * page_size:
+            status |= CHECK_LENGTH
+        clamped.append(min(max(c, 0), max_pages * page_size))
+    for b, c in enumerate(clamped):
+        for p in range(max_pages):
+            if p * page_size < c and not 0 <= bt[b, p] < num_pages:
+                status |= CHECK_PAGE
+    if tasks is not None:
+        want_tasks, want_offsets, want_n = build_queue(clamped, Hkv, split_tokens)
+        n = int(np.asarray(n_tasks).reshape(-1)[0])
+        given = np.asarray(tasks, dtype=np.int64).reshape(-1, 4)
+        if (not 0 <= n <= capacity or n != want_n
+                or not np.array_equal(np.asarray(group_offsets, dtype=np.int64), want_offsets)
+                or not np.array_equal(given[:n], want_tasks)):
+            status |= CHECK_QUEUE
+    return status

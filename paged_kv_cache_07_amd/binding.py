@@ -70,6 +70,7 @@ _SIGS = {
     "kvpage_debug_gather_offsets": (ctypes.c_int, [_S, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "kvpage_choose_split": (ctypes.c_int32, [_S, _P, ctypes.c_int32]),
     "kvpage_append_kv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "kvpage_check_inputs": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "kvpage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -161,6 +162,18 @@ def kvpage_append_kv(shape, k_new, v_new, k_pool, v_pool, block_tables, ctx_lens
         ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
         _ptr(block_tables), _ptr(ctx_lens), _ptr(ctx_lens_out), _ptr(free_pages),
         _ptr(free_count), _ptr(free_count_out), _ptr(status), _stream(stream)))
+
+
+KVPAGE_CHECK_LENGTH, KVPAGE_CHECK_PAGE, KVPAGE_CHECK_QUEUE = 1, 2, 4
+
+
+def kvpage_check_inputs(shape, ctx_lens, block_tables, tasks, group_offsets, n_tasks, capacity,
+                        status, stream=None):
+    """Debug checks of the decode preconditions; ``tasks``, ``group_offsets`` and
+    ``n_tasks`` may all be None.  Writes the KVPAGE_CHECK_* bits to ``status``."""
+    return _check("kvpage_check_inputs", lib().kvpage_check_inputs(
+        ctypes.byref(shape), _ptr(ctx_lens), _ptr(block_tables), _ptr(tasks),
+        _ptr(group_offsets), _ptr(n_tasks), int(capacity), _ptr(status), _stream(stream)))
 
 
 def kvpage_workspace_bytes(shape: kvpage_shape, capacity: int) -> int:

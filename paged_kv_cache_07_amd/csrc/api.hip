@@ -26,6 +26,9 @@ hipError_t launch_merge(const kvpage_shape&, const int32_t*, int32_t, const void
 hipError_t launch_merge_finish(const kvpage_shape&, const kvpage_budget&, const void*,
                                const int32_t*, const int32_t*, int32_t, const void*, void*, float*,
                                hipStream_t);
+hipError_t launch_check_inputs(const kvpage_shape&, const int32_t*, const int32_t*,
+                               const kvpage_task*, const int32_t*, const int32_t*, int32_t, int32_t*,
+                               hipStream_t);
 hipError_t launch_page_mass(const kvpage_shape&, const kvpage_budget&, const void*, const float*,
                             const int32_t*, const int32_t*, int32_t, const void*, hipStream_t);
 
@@ -128,6 +131,21 @@ int64_t kvpage_workspace_bytes(const kvpage_shape* s, int32_t capacity) {
   if (st == KVPAGE_OK) st = check_capacity(s, capacity);
   if (st != KVPAGE_OK) return st;
   return (int64_t)ws_bytes(capacity, s->Hq / s->Hkv, s->d);
+}
+
+int kvpage_check_inputs(const kvpage_shape* s, const int32_t* ctx_lens,
+                        const int32_t* block_tables, const kvpage_task* tasks,
+                        const int32_t* group_offsets, const int32_t* n_tasks, int32_t capacity,
+                        int32_t* status, hipStream_t stream) {
+  KV_TRY(check_shape(s));
+  if (!ctx_lens || !block_tables || !status) return KVPAGE_ERR_INVALID_ARG;
+  const bool queue = tasks || group_offsets || n_tasks;
+  if (queue) {
+    if (!tasks || !group_offsets || !n_tasks) return KVPAGE_ERR_INVALID_ARG;
+    KV_TRY(check_capacity(s, capacity));
+  }
+  return status_of(launch_check_inputs(*s, ctx_lens, block_tables, queue ? tasks : nullptr,
+                                       group_offsets, n_tasks, capacity, status, stream));
 }
 
 int kvpage_build_queue(const kvpage_shape* s, const int32_t* ctx_lens, kvpage_task* tasks,

@@ -228,3 +228,20 @@ def test_misaligned_buffers_are_rejected():
     assert rc == K.KVPAGE_ERR_INVALID_ARG           # out
     assert lib.kvpage_merge_splits(ctypes.byref(s), good, cap, ctypes.c_void_p(4096 + 8), good,
                                    good, None) == K.KVPAGE_ERR_INVALID_ARG
+
+
+def test_check_inputs_rejects_bad_arguments():
+    """Null buffers, a queue given in part, or a capacity below the queue
+    capacity are refused before anything is enqueued (no GPU needed)."""
+    lib = K.lib()
+    s = K.make_shape(2, 8, 2, 64, 16, 64, 4, 10, "f16", 0.125)
+    cap = K.kvpage_queue_capacity(s)
+    d = ctypes.c_void_p(16)
+    bad = K.KVPAGE_ERR_INVALID_ARG
+    assert lib.kvpage_check_inputs(ctypes.byref(s), None, d, None, None, None, 0, d, None) == bad
+    assert lib.kvpage_check_inputs(ctypes.byref(s), d, None, None, None, None, 0, d, None) == bad
+    assert lib.kvpage_check_inputs(ctypes.byref(s), d, d, None, None, None, 0, None, None) == bad
+    assert lib.kvpage_check_inputs(ctypes.byref(s), d, d, d, None, d, cap, d, None) == bad
+    assert lib.kvpage_check_inputs(ctypes.byref(s), d, d, d, d, d, cap - 1, d, None) \
+        == K.KVPAGE_ERR_CAPACITY
+    assert lib.kvpage_check_inputs(None, d, d, None, None, None, 0, d, None) == bad

@@ -469,3 +469,76 @@ def test_split_partials_merged_by_lse_equal_the_full_softmax(split):
             O = sum(np.exp(p[0] - M) * p[2] for p in ps) / L
             np.testing.assert_allclose(O, out[b, h], rtol=1e-12, atol=1e-14)
             assert abs(M + np.log(L) - lse[b, h]) <= 1e-12 * max(1.0, abs(lse[b, h]))
+
+
+# ---------------------------------------------------------- input checks ---
+
+def _tiny_check_case():
+    # Two sequences of 37 and 0 tokens, rows of 4 pages, pool of 10 pages,
+    # one KV head, 16-token splits.  The queue written out by hand.
+    ctx = [37, 0]
+    bt = np.array([[3, 7, 1, -1], [-1, 99, -1, -1]], dtype=np.int32)   # unused cells hold junk
+    tasks = np.array([[0, 0, 0, 16], [0, 0, 16, 32], [0, 0, 32, 37], [9, 9, 9, 9]], dtype=np.int32)
+    go = np.array([0, 3, 3], dtype=np.int32)
+    return ctx, bt, tasks, go
+
+
+def test_check_inputs_hand_worked_clean_case():
+    """Junk in table cells no sequence uses and queue rows past n_tasks is
+    allowed: the status is 0."""
+    ctx, bt, tasks, go = _tiny_check_case()
+    assert kvref.check_inputs(ctx, bt, 10, 16, 1, 16) == 0
+    assert kvref.check_inputs(ctx, bt, 10, 16, 1, 16, capacity=8, tasks=tasks, group_offsets=go,
+                              n_tasks=[3]) == 0
+
+
+@pytest.mark.parametrize("case,want", [
+    ("negative length", kvref.CHECK_LENGTH),
+    ("length past the row", kvref.CHECK_LENGTH | kvref.CHECK_QUEUE),
+    ("used page id = num_pages", kvref.CHECK_PAGE),
+    ("used page id negative", kvref.CHECK_PAGE),
+    ("task end off by one", kvref.CHECK_QUEUE),
+    ("tasks swapped", kvref.CHECK_QUEUE),
+    ("n_tasks one more", kvref.CHECK_QUEUE),
+    ("n_tasks past capacity", kvref.CHECK_QUEUE),
+    ("group offset moved", kvref.CHECK_QUEUE),
+])
+def test_check_inputs_flags_each_violation(case, want):
+    """Each kind of violation sets its own bit (a length past the row is
+    clamped, so the hand-written queue no longer matches either)."""
+    ctx, bt, tasks, go = _tiny_check_case()
+    n = [3]
+    cap = 8
+    if case == "negative length":
+        ctx = [37, -1]
+    elif case == "length past the row":
+        ctx = [65, 0]
+        bt[0, 3] = 5   # clamped to 64 tokens, the row's fourth page is now used
+    elif case == "used page id = num_pages":
+        bt[0, 2] = 10
+    elif case == "used page id negative":
+        bt[0, 0] = -1
+    elif case == "task end off by one":
+        tasks[2, 3] = 36
+    elif case == "tasks swapped":
+        tasks[[0, 1]] = tasks[[1, 0]]
+    elif case == "n_tasks one more":
+        n = [4]
+    elif case == "n_tasks past capacity":
+        cap = 2
+    elif case == "group offset moved":
+        go[1] = 2
+    got = kvref.check_inputs(ctx, bt, 10, 16, 1, 16, capacity=cap, tasks=tasks, group_offsets=go,
+                             n_tasks=n)
+    assert got == want, (case, got)
+
+
+def test_check_inputs_accepts_every_workload_queue():
+    """The queue build_queue gives for a workload's own lengths, with its
+    tables, passes every check."""
+    for name, div in (("tiny", 1), ("b8_bimodal", 64), ("b64_prefix", 32)):
+        wl = W.make(name, ctx_divisor=div) if div > 1 else W.make(name)
+        tasks, go, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
+        assert kvref.check_inputs(wl.ctx_lens, wl.block_tables, wl.num_pages, wl.page_size, wl.Hkv,
+                                  wl.split_tokens, capacity=max(n, 1), tasks=tasks,
+                                  group_offsets=go, n_tasks=[n]) == 0
