@@ -489,8 +489,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       spec.npg = min(pps, p.max_pages - spec.lp0);
       // The length first, then page ids and rows; the tiles wait for the
       // page ids (and so for the length issued before them), the operand for
-      // the rows.  Measured against page ids first: 0.2 us faster at one
-      // 32K sequence, the same within noise elsewhere.
+      // the rows.  Issuing the page ids first measured no better (within
+      // 0.2 us either way at one 32K sequence).
       raw_len = load_length(p.ctx_lens, p.B, lane);
       __builtin_amdgcn_sched_barrier(0);
       ids_spec = p.block_tables[min(spec.lp0 + lane, p.max_pages - 1)];
