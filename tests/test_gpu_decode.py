@@ -485,3 +485,34 @@ def test_stream_kv_changes_no_bits(case, one_call):
     for key in ("tasks", "group_offsets", "out_bits", "lse", "mass", "page_max", "s_next"):
         assert np.array_equal(a[key], b[key]), key
     compare_step(b, oracle_step(wl), label=case)
+
+
+@pytest.mark.parametrize("Hq,Hkv,d,dtype,ctx,extra_pages,split", [
+    (64, 8, 128, "bf16", 5000, 0, 256),   # G = 8, bf16
+    (8, 2, 64, "f16", 3000, 2, 128),      # d = 64, last split shorter than the table's
+    (8, 8, 64, "bf16", 700, 0, 64),       # G = 1, 4-page instance
+    (16, 2, 128, "f16", 2000, 20, 32),    # table wider by more than a split: predictions fail
+])
+def test_one_sequence_prediction_across_instances(Hq, Hkv, d, dtype, ctx, extra_pages, split):
+    """The predicting instance for other head groupings, head sizes, dtypes
+    and split lengths: bit for bit against the separate calls and within
+    tolerance of the oracle, with and without budgeting and streaming."""
+    from paged_kv_cache_07_amd.device import DecodeStep
+    max_pages = -(-ctx // 16) + extra_pages
+    wl = W.custom([ctx], Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, seed=60 + ctx % 89, max_pages=max_pages)
+    wl.s_prev = np.random.default_rng(10).standard_normal(wl.s_prev.shape).astype(np.float32)
+    ref = oracle_step(wl, split_tokens=split)
+    for budget, stream_kv in ((True, True), (False, True), (True, False)):
+        say("predict-inst", Hq, Hkv, d, dtype, ctx, "table", max_pages, "split", split,
+            "budget", budget, "stream", stream_kv)
+        a = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
+        a.run()
+        ra = a.results()
+        b = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
+        b.step()
+        rb = b.results()
+        keys = ["out_bits", "lse", "tasks", "group_offsets"] + (
+            ["mass", "page_max", "s_next"] if budget else [])
+        for key in keys:
+            assert np.array_equal(ra[key], rb[key]), key
+        compare_step(rb, ref, budget=budget, label=f"{Hq}/{Hkv} d{d} {dtype} ctx{ctx} S{split}")
