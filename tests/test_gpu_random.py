@@ -53,7 +53,9 @@ def _draw(seed):
     return wl, one_call, budget, stream_kv
 
 
-@pytest.mark.parametrize("seed", range(4000, 4024))
+# 5039, 5075 and 5148: bfloat16 with 16-token splits, where a weight rounded
+# once to bfloat16 had put 1-3 outputs past the tolerance.
+@pytest.mark.parametrize("seed", list(range(4000, 4024)) + [5039, 5075, 5148])
 def test_random_config_matches_oracle(seed):
     from paged_kv_cache_07_amd.device import DecodeStep
     wl, one_call, budget, stream_kv = _draw(seed)
