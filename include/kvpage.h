@@ -19,9 +19,10 @@
  *     scaled summary-key dot product on every page.
  *
  * Around the step: kvpage_append_kv is the step before it (append one token
- * per sequence, taking a page from a free list at a page boundary), and
+ * per sequence, taking a page from a free list at a page boundary),
  * kvpage_choose_split is a host-side policy that picks the split size for a
- * batch's context lengths.
+ * batch's context lengths, and kvpage_check_inputs reports violated
+ * preconditions of the integer inputs (debug checks).
  *
  * Problem statement and data layout (every tensor row-major, contiguous):
  *
