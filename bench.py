@@ -216,7 +216,14 @@ def cpu_baseline(seconds: float = 12.0):
     many = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
     n, el, used = run(many)
     n1, el1, _ = run(1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": kv * n / el / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{n} full B1 steps (ctx 32768, Hq 32, Hkv 8, d 128: queue, attention, "
                       f"page mass, summaries, page max) in {el:.1f} s, numpy fp64, {used} BLAS "
                       f"threads",
