@@ -245,3 +245,16 @@ def test_check_inputs_rejects_bad_arguments():
     assert lib.kvpage_check_inputs(ctypes.byref(s), d, d, d, d, d, cap - 1, d, None) \
         == K.KVPAGE_ERR_CAPACITY
     assert lib.kvpage_check_inputs(None, d, d, None, None, None, 0, d, None) == bad
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits non-zero with a message
+    and starts no work (no GPU needed to check this)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120, cwd=root)
+    assert res.returncode != 0
+    assert "one GPU" in res.stderr
+    assert res.stdout.strip() == ""
