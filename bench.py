@@ -356,8 +356,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "kvpage::split_attn_kernel<128, f16, budget, fused queue"
-                               + (", streaming loads" if head["stream_kv"] else "")
-                               + (", first-task prediction>" if head["B"] == 1 else ">"),
+                               + (", streaming loads>" if head["stream_kv"] else ">"),
                      "attn_ms_mean": head["attn_ms_mean"],
                      "algorithmic_bytes_per_launch": kv},
         "also": also,

@@ -22,11 +22,7 @@
 //     register layout, so no lane shuffles are needed between the two
 //     contractions;
 //   * K and V tiles stream through a ring of DEPTH register buffers, with
-//     non-temporal loads (STREAM) when the caller says no page is shared;
-//   * with one sequence (SPEC), each wavefront requests its first task's page
-//     ids, query rows and first tiles before the length has arrived, on the
-//     guess that the context fills the table row, and keeps them when the
-//     lengths confirm it.
+//     non-temporal loads (STREAM) when the caller says no page is shared.
 //
 // Outputs per run go to the workspace at the run's first queue position:
 // m (log2 domain), l = sum exp2(y - m) and the unnormalised o = sum
@@ -34,7 +30,6 @@
 #include <float.h>
 #include <math.h>
 
-#include <algorithm>
 #include <atomic>
 
 #include <hip/hip_ext.h>
@@ -104,11 +99,6 @@ struct AttnParams {
   const float* s_prev;
   int32_t split_tokens, B, Hq, Hkv, G, max_pages, num_pages, capacity;
   int32_t nwaves;   // wavefronts in the grid
-  // Predicting instance (fused build, one sequence): the chunk length and
-  // split count the schedule has when the context fills the table row, and
-  // 1 / spec_ns rounded to float.
-  int32_t spec_c, spec_ns;
-  float spec_rcp;
   // Division by split_tokens and by the number of wavefronts in the grid.
   DivMagic div_split, div_waves;
   const kvpage_task* tasks;
@@ -216,10 +206,9 @@ __device__ __forceinline__ SeqScan scan_lengths(int32_t raw, int B, int Hkv, int
   return q;
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM, bool SPEC>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const AttnParams p) {
-  static_assert(FUSEDQ || !SPEC, "the first-task prediction belongs to the fused queue build");
   using E = Elem<BF>;
   constexpr int KB = D / 32;   // 16x16x32 MFMAs per page for the scores
   constexpr int VD = D / 16;   // output column blocks; V halves per lane per token
@@ -466,45 +455,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   uint32_t buf[DEPTH][TW];
   u32x4 qop[KB];
   int ntask;
-  // Fused build with one sequence (SPEC): the first task of this wavefront
-  // when the context fills the table row.  Its page ids, query rows and first
-  // tiles are requested right behind the length and its operand is built
-  // before the lengths are scanned; all of it is kept if the lengths give
-  // that task.  This saves the dependent round trip from length to page ids.
-  Task spec = {0, 0, 0, 0, 0, 0, 0, 0};
-  int32_t ids_spec = 0;
   if constexpr (FUSEDQ) {
-    int32_t raw_len;
-    if constexpr (SPEC) {
-      const int pps = p.split_tokens / kPage;
-      const int ts = gw * p.spec_c;
-      // ts / spec_ns through the float reciprocal (off by at most one for
-      // operands below 2^22), corrected both ways.
-      int gs = (int)((float)ts * p.spec_rcp);
-      gs -= gs * p.spec_ns > ts ? 1 : 0;
-      gs += (gs + 1) * p.spec_ns <= ts ? 1 : 0;
-      spec.b = 0;
-      spec.g = min(max(gs, 0), p.Hkv - 1);
-      spec.lp0 = min((ts - spec.g * p.spec_ns) * pps, p.max_pages - 1);
-      spec.npg = min(pps, p.max_pages - spec.lp0);
-      // The length first, then page ids and rows; the tiles wait for the
-      // page ids (and so for the length issued before them), the operand for
-      // the rows.  Issuing the page ids first measured no better (within
-      // 0.2 us either way at one 32K sequence).
-      raw_len = load_length(p.ctx_lens, p.B, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      ids_spec = p.block_tables[min(spec.lp0 + lane, p.max_pages - 1)];
-      const Rows rows_spec = load_rows(spec);
-      __builtin_amdgcn_sched_barrier(0);   // all three leave before the wait for the page ids
-#pragma unroll
-      for (int tau = 0; tau < DEPTH; ++tau) load_tile(spec, ids_spec, tau, buf[tau]);
-      // Keep the first use of the length below these loads: hoisted above a
-      // tile, it made that tile wait for the length.
-      __builtin_amdgcn_sched_barrier(0);
-      build_operand(rows_spec, qop);
-    } else {
-      raw_len = load_length(p.ctx_lens, p.B, lane);
-    }
+    const int32_t raw_len = load_length(p.ctx_lens, p.B, lane);
     sq = scan_lengths(raw_len, p.B, p.Hkv, p.split_tokens, p.div_split, p.max_pages, lane);
     ntask = min(sq.total, p.capacity);
     if (blockIdx.x == 0 && wave == 0) {
@@ -538,22 +490,13 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   const int t_first = chunk * c;
 
   Task cur = fetch(t_first);
-  int32_t ids;
-  bool predicted = false;
-  if constexpr (SPEC) predicted = cur.b == 0 && cur.g == spec.g && cur.lp0 == spec.lp0;
-  if (predicted) {
-    // Same rows and page ids as requested above; tiles past the task's last
-    // page differ from what the loads below would give but are never read.
-    ids = lane < cur.npg ? ids_spec : 0;
-  } else {
-    // Query rows first: they arrive with the page ids, so the operand is
-    // built while the first tiles are in flight.
-    const Rows rows = load_rows(cur);
-    ids = load_page_ids(cur);
+  // Query rows first: they arrive with the page ids, so the operand is built
+  // while the first tiles are in flight.
+  const Rows rows = load_rows(cur);
+  int32_t ids = load_page_ids(cur);
 #pragma unroll
-    for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
-    build_operand(rows, qop);
-  }
+  for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
+  build_operand(rows, qop);
 
   // Run state: the running partial of consecutive tasks of one (b, g).
   int run_start = t_first;
@@ -813,10 +756,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   }
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM, bool SPEC>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
-  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, STREAM, SPEC>;
+  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, STREAM>;
   // Resident workgroups of this instance per device, found once.  Concurrent
   // first calls may both look it up; they store the same value.
   static std::atomic<int> resident_wg[64];
@@ -844,19 +787,6 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
   AttnParams a = p;
   a.nwaves = grid * kWavesPerGroup;
   a.div_waves = div_magic((uint32_t)grid * kWavesPerGroup);
-  a.spec_c = 0;
-  a.spec_ns = 1;
-  a.spec_rcp = 1.0f;
-  if (SPEC) {
-    // The schedule the kernel derives from a length of max_pages * P.
-    const int64_t ns = ((int64_t)p.max_pages * kPage + p.split_tokens - 1) / p.split_tokens;
-    const int64_t ntask = std::min<int64_t>(ns * p.Hkv, capacity);
-    const int64_t nw = (int64_t)grid * kWavesPerGroup;
-    const int64_t rounds = std::max<int64_t>(1, (ntask + nw * kRunMax - 1) / (nw * kRunMax));
-    a.spec_c = (int32_t)std::max<int64_t>(1, (ntask + nw * rounds - 1) / (nw * rounds));
-    a.spec_ns = (int32_t)ns;
-    a.spec_rcp = 1.0f / (float)ns;
-  }
   if (ev_start || ev_stop) {
     // Timestamps taken by the dispatch itself: start and end of this kernel.
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, ev_start,
@@ -875,35 +805,35 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
 #define KVPAGE_ATTN_DEPTH 2
 #endif
 
-template <bool FUSEDQ, int PPT, bool STREAM, bool SPEC>
+template <bool FUSEDQ, int PPT, bool STREAM>
 static hipError_t dispatch_ppt(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                                int max_wg) {
   constexpr int DP = KVPAGE_ATTN_DEPTH < PPT ? KVPAGE_ATTN_DEPTH : PPT;
   const bool bf = s.dtype == KVPAGE_BF16;
   if (s.d == 128) {
-    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                       : launch_one<128, true, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
-    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
-               : launch_one<128, false, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                       : launch_one<128, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+               : launch_one<128, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
   }
-  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                     : launch_one<64, true, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
-  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg)
-             : launch_one<64, false, false, DP, FUSEDQ, PPT, STREAM, SPEC>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                     : launch_one<64, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
+             : launch_one<64, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
 }
 
 // The instance with the fewest pages per task that holds one split: a task
 // issues loads for all of its instance's pages, so a short split run by the
 // 16-page instance would spend most of its loads on repeats.
-template <bool FUSEDQ, bool STREAM, bool SPEC>
+template <bool FUSEDQ, bool STREAM>
 static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                            int max_wg) {
   const int pages = s.split_tokens / kPage;
-  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, STREAM, SPEC>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, STREAM, SPEC>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return dispatch_ppt<FUSEDQ, 16, STREAM, SPEC>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return dispatch_ppt<FUSEDQ, 16, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 // Wavefronts of one resident round per compute unit (one workgroup per CU).
@@ -956,23 +886,16 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   p.c2 = s.scale * 1.4426950408889634f;
   p.inv_g = 1.0f / (float)G;
   p.nwaves = 0;
-  p.spec_c = 0;
-  p.spec_ns = 1;
-  p.spec_rcp = 1.0f;
   p.div_split = div_magic((uint32_t)s.split_tokens);
   p.div_waves = div_magic(1);
   const bool fused = tasks_out != nullptr;
   const bool bud = budget != nullptr;
   const bool stream_kv = (s.flags & KVPAGE_FLAG_STREAM_KV) != 0;
-  // One sequence: the instance that predicts each wavefront's first task.
-  if (fused && s.B == 1)
-    return stream_kv ? dispatch<true, true, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-              : dispatch<true, false, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
   if (fused)
-    return stream_kv ? dispatch<true, true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-              : dispatch<true, false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return stream_kv ? dispatch<false, true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-            : dispatch<false, false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+    return stream_kv ? dispatch<true, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+              : dispatch<true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return stream_kv ? dispatch<false, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+            : dispatch<false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 }  // namespace kvpage

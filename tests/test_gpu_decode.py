@@ -324,17 +324,15 @@ def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
 
 
 @pytest.mark.parametrize("ctx,extra_pages,split,max_wg", [
-    (32768, 0, 256, 0),    # context fills the table row: every first task as predicted
+    (32768, 0, 256, 0),    # context fills the table row (the headline shape)
     (32768, 0, 256, 3),    # the same with long wavefront runs (chunks of 15 tasks)
-    (4000, 6, 256, 0),     # same split count as a full row: predicted, last split shorter
-    (4000, 40, 256, 0),    # table wider by more than a split: predictions fail
+    (4000, 6, 256, 0),     # table wider by less than a split
+    (4000, 40, 256, 0),    # table wider by more than a split
     (1, 0, 256, 0), (17, 3, 64, 0), (257, 0, 128, 0), (5000, 0, 16, 0), (3000, 1, 32, 2)])
-def test_one_sequence_first_task_prediction(ctx, extra_pages, split, max_wg):
-    """One sequence in the one-call step: each wavefront requests its first
-    task's page ids, query rows and first tiles on the guess that the context
-    fills the table row, and keeps them only if the lengths give that task.
-    Whether the guess holds, holds with a shorter last split or fails, the
-    bits equal the separate calls (which never guess) and match the oracle."""
+def test_one_sequence_table_widths(ctx, extra_pages, split, max_wg):
+    """One sequence in the one-call step (fused queue build), with a table
+    exactly fitting the context, wider by less than a split and wider by more
+    than a split: the bits equal the separate calls and match the oracle."""
     from paged_kv_cache_07_amd import binding
     from paged_kv_cache_07_amd.device import DecodeStep
     max_pages = -(-ctx // 16) + extra_pages
@@ -342,7 +340,7 @@ def test_one_sequence_first_task_prediction(ctx, extra_pages, split, max_wg):
     wl.s_prev = np.random.default_rng(9).standard_normal(wl.s_prev.shape).astype(np.float32)
     ref = oracle_step(wl, split_tokens=split)
     for budget, stream_kv in ((True, True), (False, False)):
-        say("predict", ctx, "table", max_pages, "split", split, "max_wg", max_wg,
+        say("one-seq", ctx, "table", max_pages, "split", split, "max_wg", max_wg,
             "budget", budget, "stream", stream_kv)
         a = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
         a.run()
@@ -489,21 +487,22 @@ def test_stream_kv_changes_no_bits(case, one_call):
 
 @pytest.mark.parametrize("Hq,Hkv,d,dtype,ctx,extra_pages,split", [
     (64, 8, 128, "bf16", 5000, 0, 256),   # G = 8, bf16
-    (8, 2, 64, "f16", 3000, 2, 128),      # d = 64, last split shorter than the table's
+    (8, 2, 64, "f16", 3000, 2, 128),      # d = 64, table wider by less than a split
     (8, 8, 64, "bf16", 700, 0, 64),       # G = 1, 4-page instance
-    (16, 2, 128, "f16", 2000, 20, 32),    # table wider by more than a split: predictions fail
+    (16, 2, 128, "f16", 2000, 20, 32),    # table wider by more than a split
 ])
-def test_one_sequence_prediction_across_instances(Hq, Hkv, d, dtype, ctx, extra_pages, split):
-    """The predicting instance for other head groupings, head sizes, dtypes
-    and split lengths: bit for bit against the separate calls and within
-    tolerance of the oracle, with and without budgeting and streaming."""
+def test_one_sequence_across_instances(Hq, Hkv, d, dtype, ctx, extra_pages, split):
+    """One sequence in the one-call step for other head groupings, head
+    sizes, dtypes and split lengths: bit for bit against the separate calls
+    and within tolerance of the oracle, with and without budgeting and
+    streaming."""
     from paged_kv_cache_07_amd.device import DecodeStep
     max_pages = -(-ctx // 16) + extra_pages
     wl = W.custom([ctx], Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, seed=60 + ctx % 89, max_pages=max_pages)
     wl.s_prev = np.random.default_rng(10).standard_normal(wl.s_prev.shape).astype(np.float32)
     ref = oracle_step(wl, split_tokens=split)
     for budget, stream_kv in ((True, True), (False, True), (True, False)):
-        say("predict-inst", Hq, Hkv, d, dtype, ctx, "table", max_pages, "split", split,
+        say("one-seq-inst", Hq, Hkv, d, dtype, ctx, "table", max_pages, "split", split,
             "budget", budget, "stream", stream_kv)
         a = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
         a.run()
