@@ -188,48 +188,108 @@ def time_append(name: str, calls: int, flush: bool):
             "status": int(ds.append_status.item()), "B": wl.B}
 
 
+# The oracle baseline spreads whole (sequence, KV head) groups over worker
+# processes; each worker builds the same seeded workload once and runs the
+# oracle unchanged on the groups it is handed.
+_ORACLE_WL = None
+
+
+def _oracle_worker_init(name: str):
+    global _ORACLE_WL
+    from threadpoolctl import threadpool_limits
+
+    from paged_kv_cache_07_amd import workloads as W
+    threadpool_limits(limits=1)
+    _ORACLE_WL = W.make(name)
+
+
+def _oracle_groups(groups):
+    """The oracle's step for the query heads of ``groups`` [(b, g), ...]:
+    their attention rows, page mass and summary page maxima."""
+    from oracle import kvref
+    wl = _ORACLE_WL
+    rows = [(b, g * wl.G + i) for b, g in groups for i in range(wl.G)]
+    r = kvref.decode_step(wl, rows=rows)
+    return [(b, g, r["out"][b, g * wl.G:(g + 1) * wl.G], r["lse"][b, g * wl.G:(g + 1) * wl.G],
+             r["mass"][b, g * wl.G:(g + 1) * wl.G], r["page_max"][:, b, g]) for b, g in groups]
+
+
 def cpu_baseline(seconds: float = 12.0):
-    """The fp64 oracle on the host: full B1 steps repeated for ~``seconds``,
-    with the BLAS thread pool at the host's share of cores (OMP_NUM_THREADS,
-    else all), then once more on one thread."""
-    from threadpoolctl import threadpool_info, threadpool_limits
+    """The fp64 oracle on the host: full B1 steps repeated for ~``seconds``.
+
+    Multi-core: the step's (sequence, KV head) groups are spread over worker
+    processes (one BLAS thread each; as many processes as groups, at most the
+    host's share of cores), the queue is built in the parent and every
+    group's rows are gathered back into whole-step arrays.  Then the same
+    steps in one process on one thread."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
 
     from oracle import kvref
     from paged_kv_cache_07_amd import workloads as W
 
-    wl = W.make("b1")
+    name = "b1"
+    wl = W.make(name)
     kv = W.kv_bytes(wl)
+    groups = [(b, g) for b in range(wl.B) for g in range(wl.Hkv)]
+    share = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    nproc = max(1, min(share, len(groups)))
+    items = [groups[i::nproc] for i in range(nproc)]
 
-    def run(threads):
+    def whole_step(pool):
+        kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
+        out = np.empty((wl.B, wl.Hq, wl.d))
+        lse = np.empty((wl.B, wl.Hq))
+        mass = np.empty((wl.B, wl.Hq, wl.max_pages))
+        pmax = np.empty((2, wl.B, wl.Hkv, wl.max_pages))
+        for part in pool.map(_oracle_groups, items):
+            for b, g, o, l, m, pm in part:
+                out[b, g * wl.G:(g + 1) * wl.G] = o
+                lse[b, g * wl.G:(g + 1) * wl.G] = l
+                mass[b, g * wl.G:(g + 1) * wl.G] = m
+                pmax[:, b, g] = pm
+        kvref.update_summaries(wl.q, wl.s_prev, wl.Hkv, wl.alpha_fast, wl.alpha_slow, wl.dtype)
+        return out
+
+    with mp.get_context("spawn").Pool(nproc, initializer=_oracle_worker_init,
+                                      initargs=(name,)) as pool:
+        whole_step(pool)                       # warm-up: workers have built the inputs
         n = 0
-        with threadpool_limits(limits=threads):
-            used = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
-            t0 = time.perf_counter()
-            while True:
-                kvref.decode_step(wl)
-                n += 1
-                el = time.perf_counter() - t0
-                if el >= seconds:
-                    break
-        return n, el, used
+        t0 = time.perf_counter()
+        while True:
+            whole_step(pool)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
 
-    many = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
-    n, el, used = run(many)
-    n1, el1, _ = run(1)
+    n1 = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            kvref.decode_step(wl)
+            n1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= seconds:
+                break
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": kv * n / el / 1e9, "unit": "GB/s", "cores": used, "kind": "oracle",
+    return {"value": kv * n / el / 1e9, "unit": "GB/s", "cores": nproc, "kind": "oracle",
             "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{n} full B1 steps (ctx 32768, Hq 32, Hkv 8, d 128: queue, attention, "
-                      f"page mass, summaries, page max) in {el:.1f} s, numpy fp64, {used} BLAS "
-                      f"threads",
+                      f"page mass, summaries, page max) in {el:.1f} s, numpy fp64, "
+                      f"{nproc} worker processes x 1 BLAS thread, (sequence, KV head) groups "
+                      f"spread over them",
             "steps_per_s": n / el,
             "single_thread": {"value": kv * n1 / el1 / 1e9, "unit": "GB/s", "cores": 1,
-                              "steps_per_s": n1 / el1}}
+                              "steps_per_s": n1 / el1,
+                              "sample": f"{n1} full B1 steps in {el1:.1f} s, one process, "
+                                        f"one BLAS thread"}}
 
 
 def main():

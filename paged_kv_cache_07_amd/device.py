@@ -74,6 +74,24 @@ class DecodeStep:
             self._make_budget()
         else:
             self.budget = None
+        self.scribble()
+
+    def scribble(self):
+        """Fill every buffer the library writes (queue, workspace, outputs)
+        with NaN or junk, so that an entry a kernel fails to write cannot pass
+        a comparison as a leftover zero."""
+        torch = _torch()
+        self.tasks.fill_(-7)
+        self.group_offsets.fill_(-7)
+        self.n_tasks.fill_(-7)
+        self.workspace.fill_(0xFF)          # NaN floats, header word -1
+        self.out.fill_(float("nan"))
+        self.lse.fill_(float("nan"))
+        if self.use_budget:
+            self.page_mass.fill_(float("nan"))
+            self.page_max.fill_(float("nan"))
+            self.s_next.fill_(float("nan"))
+        torch.cuda.synchronize(self.device)
 
     def _make_budget(self):
         self.budget = K.make_budget(self.page_mass, self.s_prev, self.s_next, self.page_max,

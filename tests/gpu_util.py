@@ -74,6 +74,15 @@ def sample_rows(wl, n, seed=0):
     return sorted(rows)
 
 
+def group_rows(wl, extra=0, seed=0):
+    """One query head of every (sequence, KV head) group (the head index
+    rotates with b + g), plus ``extra`` sampled rows."""
+    rows = {(b, g * wl.G + (b + g) % wl.G) for b in range(wl.B) for g in range(wl.Hkv)}
+    if extra:
+        rows |= set(sample_rows(wl, extra, seed))
+    return sorted(rows)
+
+
 def oracle_step(wl, rows=None, q=None, s_prev=None, split_tokens=None):
     if split_tokens is not None and split_tokens != wl.split_tokens:
         import dataclasses
