@@ -44,7 +44,8 @@
  * during the call; every other pointer is a DEVICE pointer.  Calls enqueue
  * work on `stream` and return without synchronizing; the library never
  * allocates, frees or synchronizes and keeps no per-call state (only a
- * per-device count of resident workgroups, found on first use).  Calls that
+ * per-device count of resident workgroups, found on first use, and the static
+ * device workspace of kvpage_decode_step_noalloc).  Calls that
  * may run at the same time (other streams) need their own queue, workspace
  * and output buffers; inputs may be shared.  Every call can be captured in
  * a HIP graph: it enqueues kernels only (no memset, copy or allocation).
@@ -84,7 +85,8 @@ typedef enum {
   KVPAGE_ERR_INVALID_ARG = -1, /* null pointer, inconsistent or out-of-range shape */
   KVPAGE_ERR_UNSUPPORTED = -2, /* valid shape the library has no kernel for       */
   KVPAGE_ERR_CAPACITY = -3,    /* task capacity below kvpage_queue_capacity()     */
-  KVPAGE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed       */
+  KVPAGE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed       */
+  KVPAGE_ERR_SCRATCH = -5      /* workspace larger than the library's static one  */
 } kvpage_status;
 
 typedef enum { KVPAGE_F16 = 0, KVPAGE_BF16 = 1 } kvpage_dtype;
@@ -209,6 +211,34 @@ int kvpage_decode_step(const kvpage_shape* shape, const void* q, const void* k_p
                        kvpage_task* tasks, int32_t* group_offsets, int32_t* n_tasks,
                        int32_t capacity, void* workspace, const kvpage_budget* budget, void* out,
                        float* lse, const kvpage_launch_opts* opts, hipStream_t stream);
+
+/* Bytes of the static device workspace of kvpage_decode_step_noalloc. */
+#define KVPAGE_NOALLOC_WORKSPACE_BYTES (64u << 20)
+
+/* kvpage_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same kernels, with the workspace taken from a static
+ * device array of KVPAGE_NOALLOC_WORKSPACE_BYTES (64 MiB) that the library
+ * holds on every device it runs on until the process ends; the caller still
+ * passes inputs, queue and outputs.  Arguments are those of
+ * kvpage_decode_step without `workspace`; outputs are bit for bit those of
+ * kvpage_decode_step.  The workspace is the current device's (the stream
+ * must belong to it).  Nothing in it has to start at zero, so nothing is
+ * cleared; every call on a device shares that device's array and leaves it
+ * holding the last call's split partials, so calls that may overlap on one
+ * device (other streams, other threads) race and must be serialised by the
+ * caller.  Returns KVPAGE_ERR_SCRATCH, enqueueing nothing, when
+ * kvpage_workspace_bytes(shape, capacity) exceeds the static size (for
+ * example B = 1, Hq = 32, Hkv = 8, d = 128, 2048 pages of 16 tokens, split
+ * 256: 2.1 MB; 8 sequences of up to 65536 tokens at split 256: 34 MB).  The
+ * call allocates and frees nothing; its first call on a device looks up that
+ * device's address of the array (hipGetSymbolAddress). */
+int kvpage_decode_step_noalloc(const kvpage_shape* shape, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               const int32_t* ctx_lens, kvpage_task* tasks,
+                               int32_t* group_offsets, int32_t* n_tasks, int32_t capacity,
+                               const kvpage_budget* budget, void* out, float* lse,
+                               const kvpage_launch_opts* opts, hipStream_t stream);
 
 /* Finish the budgeting outputs after kvpage_decode_attn ran with the same
  * budget, queue and workspace: page_mass[b,h,p] becomes the softmax weight

@@ -19,6 +19,8 @@ KVPAGE_ERR_INVALID_ARG = -1
 KVPAGE_ERR_UNSUPPORTED = -2
 KVPAGE_ERR_CAPACITY = -3
 KVPAGE_ERR_HIP = -4
+KVPAGE_ERR_SCRATCH = -5
+KVPAGE_NOALLOC_WORKSPACE_BYTES = 64 << 20
 KVPAGE_F16 = 0
 KVPAGE_BF16 = 1
 
@@ -67,6 +69,9 @@ _SIGS = {
     "kvpage_page_mass": (ctypes.c_int, [_S, _B, _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "kvpage_decode_step": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                           _B, _P, _P, ctypes.POINTER(kvpage_launch_opts), _P]),
+    "kvpage_decode_step_noalloc": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                  ctypes.c_int32, _B, _P, _P,
+                                                  ctypes.POINTER(kvpage_launch_opts), _P]),
     "kvpage_debug_gather_offsets": (ctypes.c_int, [_S, _P, _P, _P, ctypes.c_int32, _P, _P]),
     "kvpage_choose_split": (ctypes.c_int32, [_S, _P, ctypes.c_int32]),
     "kvpage_append_kv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -225,6 +230,16 @@ def kvpage_decode_step(shape, q, k_pool, v_pool, block_tables, ctx_lens, tasks, 
         ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         _ptr(ctx_lens), _ptr(tasks), _ptr(group_offsets), _ptr(n_tasks), capacity,
         _ptr(workspace), None if budget is None else ctypes.byref(budget), _ptr(out), _ptr(lse),
+        None if opts is None else ctypes.byref(opts), _stream(stream)))
+
+
+def kvpage_decode_step_noalloc(shape, q, k_pool, v_pool, block_tables, ctx_lens, tasks,
+                               group_offsets, n_tasks, capacity, budget, out, lse, opts=None,
+                               stream=None):
+    return _check("kvpage_decode_step_noalloc", lib().kvpage_decode_step_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        _ptr(ctx_lens), _ptr(tasks), _ptr(group_offsets), _ptr(n_tasks), capacity,
+        None if budget is None else ctypes.byref(budget), _ptr(out), _ptr(lse),
         None if opts is None else ctypes.byref(opts), _stream(stream)))
 
 

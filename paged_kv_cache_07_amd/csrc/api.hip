@@ -4,7 +4,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kvpage_common.h"
+
+// Workspace of kvpage_decode_step_noalloc: one copy per device, at its own
+// address on each.  Host code never passes this name to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[KVPAGE_NOALLOC_WORKSPACE_BYTES];
 
 namespace kvpage {
 hipError_t launch_build_queue(const kvpage_shape&, const int32_t*, kvpage_task*, int32_t, int32_t*,
@@ -107,6 +115,23 @@ int validate_attn(const kvpage_shape* s, const void* q, const void* k_pool, cons
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(workspace, 16))
     return KVPAGE_ERR_INVALID_ARG;
   if (budget) KV_TRY(check_budget(budget));
+  return KVPAGE_OK;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device and kept.  Concurrent first calls may both look it up;
+// they store the same address.
+int scratch_address(void** out) {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVPAGE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return KVPAGE_ERR_UNSUPPORTED;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVPAGE_ERR_HIP;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
   return KVPAGE_OK;
 }
 
@@ -234,6 +259,23 @@ int kvpage_decode_step(const kvpage_shape* s, const void* q, const void* k_pool,
   return status_of(launch_merge(*s, group_offsets, capacity, workspace, out, lse, stream));
 }
 
+int kvpage_decode_step_noalloc(const kvpage_shape* s, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               const int32_t* ctx_lens, kvpage_task* tasks,
+                               int32_t* group_offsets, int32_t* n_tasks, int32_t capacity,
+                               const kvpage_budget* budget, void* out, float* lse,
+                               const kvpage_launch_opts* opts, hipStream_t stream) {
+  KV_TRY(check_shape(s));
+  KV_TRY(check_supported(s));
+  KV_TRY(check_capacity(s, capacity));
+  if (ws_bytes(capacity, s->Hq / s->Hkv, s->d) > (size_t)KVPAGE_NOALLOC_WORKSPACE_BYTES)
+    return KVPAGE_ERR_SCRATCH;
+  void* ws = nullptr;
+  KV_TRY(scratch_address(&ws));
+  return kvpage_decode_step(s, q, k_pool, v_pool, block_tables, ctx_lens, tasks, group_offsets,
+                            n_tasks, capacity, ws, budget, out, lse, opts, stream);
+}
+
 int kvpage_page_mass(const kvpage_shape* s, const kvpage_budget* budget, const void* q,
                      const float* lse, const int32_t* ctx_lens, const int32_t* group_offsets,
                      int32_t capacity, const void* workspace, hipStream_t stream) {
@@ -335,6 +377,7 @@ const char* kvpage_status_string(int status) {
     case KVPAGE_ERR_UNSUPPORTED: return "unsupported shape";
     case KVPAGE_ERR_CAPACITY: return "task capacity too small";
     case KVPAGE_ERR_HIP: return "HIP runtime error";
+    case KVPAGE_ERR_SCRATCH: return "workspace larger than the static no-allocation workspace";
     default: return "unknown status";
   }
 }

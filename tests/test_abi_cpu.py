@@ -258,3 +258,21 @@ def test_bench_refuses_more_than_one_gpu():
     assert res.returncode != 0
     assert "one GPU" in res.stderr
     assert res.stdout.strip() == ""
+
+
+def test_noalloc_step_refuses_a_workspace_past_its_static_size():
+    """kvpage_decode_step_noalloc checks the workspace size against its
+    static array before touching the device: 64 x 8 heads x 64 splits x G 8
+    needs 136 MB, past the 64 MiB array."""
+    lib = K.lib()
+    s = K.make_shape(64, 64, 8, 128, 16, 256, 1024, 100000, "bf16", 128 ** -0.5, 0)
+    cap = K.kvpage_queue_capacity(s)
+    assert K.kvpage_workspace_bytes(s, cap) > K.KVPAGE_NOALLOC_WORKSPACE_BYTES
+    dummy = ctypes.c_void_p(256)
+    rc = lib.kvpage_decode_step_noalloc(ctypes.byref(s), dummy, dummy, dummy, dummy, dummy, dummy,
+                                        dummy, dummy, cap, None, dummy, dummy, None, None)
+    assert rc == K.KVPAGE_ERR_SCRATCH
+    assert "static" in K.status_string(rc)
+    small = K.make_shape(1, 32, 8, 128, 16, 256, 2048, 4096, "f16", 128 ** -0.5, 0)
+    assert K.kvpage_workspace_bytes(small, K.kvpage_queue_capacity(small)) \
+        <= K.KVPAGE_NOALLOC_WORKSPACE_BYTES
