@@ -148,8 +148,10 @@ int32_t kvpage_queue_capacity(const kvpage_shape* shape);
  * kvpage_page_mass / kvpage_decode_step need for `capacity` tasks: the split
  * partials (an unnormalised output row, a reference max and a sum of
  * exponentials per query head for each run of consecutive tasks of one
- * (sequence, KV head) that a wavefront processed) and a small header.
- * Negative kvpage_status on error. */
+ * (sequence, KV head) that a wavefront processed) and a small header.  It
+ * does not depend on budgeting: raw page sums and page maxima go straight
+ * into the caller's page_mass / page_max buffers.  Negative kvpage_status on
+ * error. */
 int64_t kvpage_workspace_bytes(const kvpage_shape* shape, int32_t capacity);
 
 /* Build the compact task queue (PersistentKV summary, Summary: only
@@ -177,11 +179,22 @@ int kvpage_split_attn(const kvpage_shape* shape, const void* q, const void* k_po
 
 /* Log-sum-exp merge of the split partials of each (sequence, query head),
  * over its group's task range in split order: out = sum_j w_j o_j / sum_j w_j
- * l_j with w_j = exp(m_j - max m), lse = max m + ln(sum_j w_j l_j). */
+ * l_j with w_j = exp(m_j - max m), lse = max m + ln(sum_j w_j l_j).  The
+ * pages do not give the merge; splitting a sequence's tokens into tasks
+ * (PersistentKV summary, Method: sequence-split tasks) needs one, and this is
+ * the standard flash-decoding log-sum-exp combination, which gives the
+ * softmax over the whole context up to rounding.  out: [B, Hq, d] in q's
+ * dtype; lse: float32 [B, Hq]; group_offsets as kvpage_build_queue wrote
+ * them; workspace as kvpage_split_attn left it. */
 int kvpage_merge_splits(const kvpage_shape* shape, const int32_t* group_offsets, int32_t capacity,
                         const void* workspace, void* out, float* lse, hipStream_t stream);
 
-/* kvpage_split_attn followed by kvpage_merge_splits on the same stream. */
+/* Decode attention over the queued tasks (PersistentKV summary, Summary:
+ * block-table decode attention for GQA, K/V tiles shared by the query heads
+ * of a KV-head group; Method: sequence-split tasks):
+ * kvpage_split_attn followed by kvpage_merge_splits on the same stream.
+ * Arguments as for those two calls; with `budget` the page values are left
+ * for kvpage_page_mass to finish. */
 int kvpage_decode_attn(const kvpage_shape* shape, const void* q, const void* k_pool,
                        const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
                        const kvpage_task* tasks, const int32_t* group_offsets,
@@ -240,17 +253,29 @@ int kvpage_decode_step_noalloc(const kvpage_shape* shape, const void* q, const v
                                const kvpage_budget* budget, void* out, float* lse,
                                const kvpage_launch_opts* opts, hipStream_t stream);
 
-/* Finish the budgeting outputs after kvpage_decode_attn ran with the same
- * budget, queue and workspace: page_mass[b,h,p] becomes the softmax weight
- * of page p (using the merged lse), entries past each sequence's last page
- * are set (mass 0, page_max -inf), and s_next is written for every (b, g),
- * including sequences with no tokens. */
+/* Finish the budgeting outputs (GrowPage, mlsanity.com entry, Abstract:
+ * page-level KV budgeting driven by dual-timescale query summaries;
+ * aitrending.vip article, Technical Details) after kvpage_decode_attn ran
+ * with the same budget, queue and workspace: page_mass[b,h,p] becomes the
+ * softmax weight of page p (using the merged lse), entries past each
+ * sequence's last page are set (mass 0, page_max -inf), and s_next is
+ * written for every (b, g), including sequences with no tokens.  The page
+ * values are addressed by logical page: page p of (b, g) lies in the task
+ * group_offsets[b*Hkv + g] + p*P/split_tokens, whose run the workspace
+ * header locates, so the queue itself is not read; `capacity` is the one the
+ * workspace was laid out for.  lse: float32 [B, Hq] as the merge wrote it;
+ * q: [B, Hq, d]; ctx_lens: [B]. */
 int kvpage_page_mass(const kvpage_shape* shape, const kvpage_budget* budget, const void* q,
                      const float* lse, const int32_t* ctx_lens, const int32_t* group_offsets,
                      int32_t capacity, const void* workspace, hipStream_t stream);
 
-/* Test support: the pool element offset each queued task reads for each of
- * its tokens, computed by the same addressing code as kvpage_split_attn.
+/* Test support (PersistentKV summary, Summary: native page tables): the pool
+ * element offset each queued task reads for each of its tokens.  It is
+ * built from kvpage_split_attn's own addressing: the (page, KV head) tile
+ * offset, then the row that the kernel's K and V lane maps load for the
+ * token's slot, after checking that those lanes' pieces lie in that row and
+ * cover its d elements exactly once (else -2).  The per-lane column split
+ * inside a row is checked only by that coverage test and by the outputs.
  * offsets: int64 [capacity, split_tokens]; slot j of task i holds the offset
  * of token tok_begin + j, or -1 past tok_end.  Rows >= n_tasks untouched. */
 int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_tables,

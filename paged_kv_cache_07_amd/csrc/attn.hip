@@ -257,10 +257,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   // Byte offsets of this lane's pieces inside one (page, head) tile.
   uint32_t koff[KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) koff[kb] = (uint32_t)(n * D + 8 * (4 * kb + r)) * 2u;
+  for (int kb = 0; kb < KB; ++kb) koff[kb] = k_piece_offset(kb, n, r, D);
   uint32_t voff[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) voff[e] = (uint32_t)((4 * r + e) * D + n * VD) * 2u;
+  for (int e = 0; e < 4; ++e) voff[e] = v_piece_offset(e, n, r, D);
 
   const char* kpool = reinterpret_cast<const char*>(p.k_pool);
   const char* vpool = reinterpret_cast<const char*>(p.v_pool);

@@ -22,10 +22,18 @@ __device__ __forceinline__ int64_t tile_offset(int32_t page, int32_t kv_head, in
   return ((int64_t)page * Hkv + kv_head) * (int64_t)(kPage * d);
 }
 
-// Element offset of logical token t of a sequence whose block-table row is bt_row.
-__device__ __forceinline__ int64_t token_offset(const int32_t* bt_row, int32_t t, int32_t kv_head,
-                                                int32_t Hkv, int32_t d) {
-  return tile_offset(bt_row[t / kPage], kv_head, Hkv, d) + (int64_t)(t % kPage) * d;
+// Lane maps of the attention kernel's tile loads (byte offsets inside one
+// (page, KV head) tile of D-element rows).  A wavefront's lane is (n, r) =
+// (lane % 16, lane / 16).
+//   K: for 16x16x32 MFMA block kb, lane (n, r) loads the 16 bytes of token n,
+//      elements 8 * (4 * kb + r) .. + 8: the MFMA's row operand (row = token).
+//   V: for row group e, lane (n, r) loads token 4 * r + e, elements n * D / 16
+//      .. + D / 16: whole rows per 16 lanes.
+__host__ __device__ inline uint32_t k_piece_offset(int kb, int n, int r, int D) {
+  return (uint32_t)(n * D + 8 * (4 * kb + r)) * 2u;
+}
+__host__ __device__ inline uint32_t v_piece_offset(int e, int n, int r, int D) {
+  return (uint32_t)((4 * r + e) * D + n * (D / 16)) * 2u;
 }
 
 // Lengths and page ids come from the caller's device data.  Every kernel
