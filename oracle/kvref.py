@@ -37,6 +37,17 @@ What is computed, and where it comes from:
   group) a fast and a slow exponential moving average of the group-mean query,
   ``s <- (1 - a) * s + a * qbar``, and per page the largest scaled dot product
   of each updated summary with the page's keys.
+* Budgeting decision -- GrowPage (mlsanity.com entry, Abstract; aitrending.vip
+  article, Technical Details: on-demand page allocation) compares the two
+  summaries' attention working sets and, at each capacity boundary, either
+  compresses within the allocation or acquires a page.  The pages give no
+  formula; the reading implemented: a working set is the smallest top set of
+  pages (by summary page score, equal scores entering together) holding at
+  least ``tau`` of the scores' softmax weight; F and S are the unions over KV
+  heads of the fast and slow sets; a sequence whose last page is full
+  acquires when ``|F| > |S|`` or no page lies outside both, else compresses
+  the page outside both with the lowest slow score (largest slow page max
+  over the KV heads; ties to the lowest page).
 
 Everything is float64.  Inputs keep the exact stored bits: float16 arrays, or
 uint16 arrays holding bfloat16 bit patterns, are widened exactly.
@@ -53,11 +64,16 @@ __all__ = [
     "update_summaries", "summary_page_max", "decode_step", "append_kv",
     "APPEND_FULL", "APPEND_NO_PAGE", "APPEND_BAD_PAGE",
     "check_inputs", "CHECK_LENGTH", "CHECK_PAGE", "CHECK_QUEUE",
+    "working_set", "budget_decision", "DECIDE_NONE", "DECIDE_ACQUIRE", "DECIDE_COMPRESS",
 ]
 
 APPEND_FULL = 1      # status bit: a sequence had no room left in its block-table row
 APPEND_NO_PAGE = 2   # status bit: the free list ran out
 APPEND_BAD_PAGE = 4  # status bit: a page id outside the pool (free list or table)
+
+DECIDE_NONE = 0      # decision: the sequence is not at a capacity boundary
+DECIDE_ACQUIRE = 1   # decision: take one more physical page
+DECIDE_COMPRESS = 2  # decision: stay within the allocation, compress the victim page
 
 CHECK_LENGTH = 1     # status bit: a length outside [0, max_pages * P]
 CHECK_PAGE = 2       # status bit: a table entry a sequence uses outside the pool
@@ -323,3 +339,76 @@ def check_inputs(ctx_lens, block_tables, num_pages: int, page_size: int, Hkv: in
                 or not np.array_equal(given[:n], want_tasks)):
             status |= CHECK_QUEUE
     return status
+
+
+def working_set(scores, tau: float):
+    """Attention working set of one summary over one sequence's pages.
+
+    ``scores``: the page scores (summary page maxima) of the sequence's
+    pages.  Their softmax gives page weights; the working set is every page
+    whose score is at or above the highest score level whose at-or-above
+    pages hold at least ``tau`` of the weight, i.e. the smallest top set by
+    score covering ``tau``, pages of equal score entering together.  Scores
+    of -inf weigh 0 (all -inf: they all tie).  Returns ``(size, level)``;
+    ``(0, inf)`` for no pages.
+    """
+    x = np.asarray(scores, dtype=np.float64)
+    if x.size == 0:
+        return 0, math.inf
+    M = np.max(x)
+    with np.errstate(invalid="ignore"):
+        w = np.where(x == M, 1.0, np.exp(x - M))
+    pi = w / np.sum(w)
+    order = np.argsort(-x, kind="stable")          # pages by score, highest first
+    xs = x[order]
+    cum = np.cumsum(pi[order])
+    ends = np.flatnonzero(np.r_[xs[1:] != xs[:-1], True])   # last page of each score level
+    hit = np.flatnonzero(cum[ends] >= tau)
+    j = ends[hit[0]] if hit.size else ends[-1]
+    return int(j + 1), float(xs[j])
+
+
+def budget_decision(page_max, ctx_lens, page_size: int, tau: float, ws_size=None):
+    """Compress-or-acquire decision of every sequence (see the header).
+
+    ``page_max``: [2, B, Hkv, max_pages] summary page maxima (0 fast, 1 slow)
+    as the step writes them; only each sequence's first ``ceil(ctx/P)``
+    pages are read.  ``ws_size`` (optional [2, B, Hkv]): take these working
+    sets (the given number of top pages by score) instead of computing them,
+    to decide from another implementation's sets.  Returns a dict with
+    ``ws_size`` and ``ws_level`` [2, B, Hkv], ``ws_union`` [2, B] (sizes of
+    F and S), ``decision`` [B] and ``victim`` [B] (-1 unless compressing).
+    """
+    pm = np.asarray(page_max, dtype=np.float64)
+    _, B, Hkv, _ = pm.shape
+    size = np.zeros((2, B, Hkv), dtype=np.int64)
+    level = np.full((2, B, Hkv), np.inf)
+    union = np.zeros((2, B), dtype=np.int64)
+    decision = np.full(B, DECIDE_NONE, dtype=np.int64)
+    victim = np.full(B, -1, dtype=np.int64)
+    for b in range(B):
+        ctx = int(ctx_lens[b])
+        npg = -(-ctx // page_size)
+        member = np.zeros((2, npg), dtype=bool)
+        for k in range(2):
+            for g in range(Hkv):
+                x = pm[k, b, g, :npg]
+                if ws_size is None:
+                    size[k, b, g], level[k, b, g] = working_set(x, tau)
+                else:
+                    n = int(ws_size[k, b, g])
+                    size[k, b, g] = n
+                    level[k, b, g] = np.sort(x)[::-1][n - 1] if n > 0 else np.inf
+                member[k] |= x >= level[k, b, g]
+        union[:, b] = member.sum(axis=1)
+        if ctx == 0 or ctx % page_size != 0:
+            continue
+        outside = np.flatnonzero(~(member[0] | member[1]))
+        if union[0, b] > union[1, b] or outside.size == 0:
+            decision[b] = DECIDE_ACQUIRE
+            continue
+        decision[b] = DECIDE_COMPRESS
+        slow = pm[1, b, :, :npg].max(axis=0)       # a page's best slow score over KV heads
+        victim[b] = min(outside, key=lambda p: (slow[p], p))
+    return {"ws_size": size, "ws_level": level, "ws_union": union,
+            "decision": decision, "victim": victim}

@@ -542,3 +542,147 @@ def test_check_inputs_accepts_every_workload_queue():
         assert kvref.check_inputs(wl.ctx_lens, wl.block_tables, wl.num_pages, wl.page_size, wl.Hkv,
                                   wl.split_tokens, capacity=max(n, 1), tasks=tasks,
                                   group_offsets=go, n_tasks=[n]) == 0
+
+
+# ------------------------------------------------ compress-or-acquire decision ---
+# GrowPage (mlsanity.com entry, Abstract; aitrending.vip article, Technical
+# Details): working sets of the fast and slow summaries, compared at each
+# capacity boundary.  Reading and hand-worked cases: tests/golden/growpage_decision.txt.
+
+import itertools  # noqa: E402
+
+import decision_cases  # noqa: E402
+
+
+@pytest.mark.parametrize("case", decision_cases.load(), ids=lambda c: c["name"])
+def test_decision_hand_worked_cases(case):
+    r = kvref.budget_decision(case["page_max"], [case["ctx"]], 16, case["tau"])
+    assert np.array_equal(r["ws_size"][:, 0], case["ws_size"])
+    assert np.array_equal(r["ws_union"][:, 0], case["union"])
+    assert r["decision"][0] == case["decision"]
+    assert r["victim"][0] == case["victim"]
+
+
+def _brute_working_set(x, tau):
+    """Smallest set of pages that is closed upward in score (a page in it
+    brings every page scoring at least as high) and holds >= tau of the
+    softmax weight, found by trying every subset."""
+    n = len(x)
+    w = [math.exp(v - max(x)) for v in x]
+    Z = sum(w)
+    best = None
+    for mask in range(1, 1 << n):
+        s = [i for i in range(n) if mask >> i & 1]
+        if any(x[j] >= x[i] and j not in s for i in s for j in range(n)):
+            continue
+        if sum(w[i] for i in s) / Z >= tau and (best is None or len(s) < len(best)):
+            best = s
+    return best
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_working_set_matches_brute_force(seed):
+    """Scores from a few integer levels (many ties); tau drawn away from every
+    achievable covered fraction so rounding cannot decide."""
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 8))
+    x = [float(v) for v in rng.integers(-3, 3, n) * 0.7]
+    w = np.exp(np.array(x) - max(x))
+    fracs = sorted({float(w[np.array(x) >= lv].sum() / w.sum()) for lv in x})
+    while True:
+        tau = float(rng.uniform(0.05, 1.0))
+        if all(abs(tau - f) > 1e-9 for f in fracs):
+            break
+    size, level = kvref.working_set(x, tau)
+    want = _brute_working_set(x, tau)
+    assert size == len(want)
+    assert level == min(x[i] for i in want)
+    assert sorted(i for i in range(n) if x[i] >= level) == sorted(want)
+
+
+def test_working_set_depends_only_on_score_differences():
+    """The weights are a softmax: shifting every score of a set by a constant
+    changes no working set (a fixed threshold on raw scores would)."""
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        x = rng.standard_normal(30) * 3
+        for c in (-50.0, 7.5, 300.0):
+            assert kvref.working_set(x + c, 0.9)[0] == kvref.working_set(x, 0.9)[0]
+
+
+def test_working_set_geometric_weights_closed_form():
+    """Scores -p ln 2 give weights 2^-p / (1 - 2^-n): the top k pages hold
+    (1 - 2^-k) / (1 - 2^-n), so the set for tau is the smallest such k."""
+    n = 12
+    x = [-p * math.log(2.0) for p in range(n)]
+    for tau in (0.3, 0.5001, 0.74, 0.76, 0.9, 0.97, 0.999):
+        k = next(k for k in range(1, n + 1)
+                 if Fraction(2 ** k - 1, 2 ** k) / Fraction(2 ** n - 1, 2 ** n) >= Fraction(tau))
+        assert kvref.working_set(x, tau)[0] == k, tau
+
+
+def test_working_set_ties_and_extremes():
+    assert kvref.working_set([1.0] * 5, 1e-6) == (5, 1.0)            # one level: all
+    assert kvref.working_set([2.0, 1.0, 1.0], 1.0)[0] == 3            # tau 1: every page
+    assert kvref.working_set([50.0, 0.0, 0.0], 0.5)[0] == 1           # a dominant page
+    assert kvref.working_set([-np.inf, 0.0, -np.inf], 0.99)[0] == 1   # -inf weighs 0
+    assert kvref.working_set([-np.inf, -np.inf], 0.5)[0] == 2         # all -inf tie
+    assert kvref.working_set([], 0.9) == (0, math.inf)
+
+
+def test_decision_from_given_working_sets_is_the_same():
+    """Deciding from the sets' sizes (another implementation's sets) gives
+    the oracle's own decision when the sizes agree."""
+    rng = np.random.default_rng(5)
+    pm = rng.standard_normal((2, 6, 3, 40)) * 2
+    ctx = np.array([640, 0, 16, 300, 48, 17])
+    a = kvref.budget_decision(pm, ctx, 16, 0.8)
+    b = kvref.budget_decision(pm, ctx, 16, 0.8, ws_size=a["ws_size"])
+    for key in ("ws_size", "ws_level", "ws_union", "decision", "victim"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_decision_rules_on_random_sequences():
+    """Every decision follows its rule: none off a boundary; acquire exactly
+    when |F| > |S| or F and S cover every page; otherwise the victim lies
+    outside both sets and no page outside them has a lower best slow score
+    (or an equal one and a lower index).  F and S are checked against the
+    union of per-head brute-force sets."""
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        B, Hkv = 4, int(rng.integers(1, 4))
+        npg_max = 7
+        pm = np.round(rng.standard_normal((2, B, Hkv, npg_max)) * 1.5, 1)
+        ctx = rng.integers(0, npg_max * 16 + 1, B)
+        ctx[rng.random(B) < 0.5] = rng.integers(0, npg_max + 1) * 16
+        tau = float(rng.choice([0.5, 0.62, 0.83, 0.95]))
+        r = kvref.budget_decision(pm, ctx, 16, tau)
+        for b in range(B):
+            npg = -(-int(ctx[b]) // 16)
+            sets, near_tie = [], False
+            for k in range(2):
+                u = set()
+                for g in range(Hkv):
+                    x = np.array(pm[k, b, g, :npg])
+                    if npg == 0:
+                        continue
+                    w = np.exp(x - x.max())
+                    if any(abs(w[x >= lv].sum() / w.sum() - tau) < 1e-9 for lv in x):
+                        near_tie = True
+                    u |= set(_brute_working_set(list(x), tau))
+                sets.append(u)
+            F, S = (set().union(set(), *[set(np.flatnonzero(pm[k, b, g, :npg] >= r["ws_level"][k, b, g]))
+                                         for g in range(Hkv)]) for k in (0, 1))
+            if not near_tie:
+                assert sets == [F, S]
+            assert r["ws_union"][0, b] == len(F) and r["ws_union"][1, b] == len(S)
+            outside = [p for p in range(npg) if p not in F and p not in S]
+            d, v = r["decision"][b], r["victim"][b]
+            if ctx[b] == 0 or ctx[b] % 16:
+                assert d == kvref.DECIDE_NONE and v == -1
+            elif len(F) > len(S) or not outside:
+                assert d == kvref.DECIDE_ACQUIRE and v == -1
+            else:
+                assert d == kvref.DECIDE_COMPRESS and v in outside
+                slow = pm[1, b, :, :npg].max(axis=0)
+                assert all((slow[v], v) <= (slow[p], p) for p in outside)
