@@ -188,6 +188,46 @@ def time_append(name: str, calls: int, flush: bool):
             "status": int(ds.append_status.item()), "B": wl.B}
 
 
+def time_decide(name: str, calls: int, flush: bool, tau: float = 0.9):
+    """kvpage_budget_decide where it runs in a serving step: right after the
+    budgeting decode step that wrote its page maxima (workload `name`, every
+    length cut back to a page boundary so that every sequence gets a
+    decision).  Per call: cache flush, the decode step, then HIP events
+    around the decision alone (both kernels)."""
+    import torch
+
+    from paged_kv_cache_07_amd import binding, workloads as W
+    from paged_kv_cache_07_amd.device import DecodeStep
+
+    wl = W.make(name)
+    ds = DecodeStep(wl, stream_kv=not wl.shares_pages())
+    ds.step()
+    dev = ds.device
+    ctx = torch.from_numpy((wl.ctx_lens // 16 * 16).astype(np.int32)).to(dev)
+    size = torch.empty((2, wl.B, wl.Hkv), dtype=torch.int32, device=dev)
+    level = torch.empty((2, wl.B, wl.Hkv), dtype=torch.float32, device=dev)
+    union = torch.empty((2, wl.B), dtype=torch.int32, device=dev)
+    dec = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    vic = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(calls + 3)]
+    for a, b in ev:       # the first three calls are warm-up
+        if flush:
+            torch.sum(flush_buf, dim=0, out=sink[0])
+        ds.step()
+        a.record()
+        binding.kvpage_budget_decide(ds.shape, ds.page_max, ctx, tau, size, level, union, dec, vic)
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_ms(b) for a, b in ev[3:]]) * 1e3
+    d = dec.cpu().numpy()
+    return {"calls": calls, "us_mean": float(us.mean()), "us_p50": float(np.median(us)),
+            "tau": tau, "B": wl.B, "Hkv": wl.Hkv, "max_pages": wl.max_pages,
+            "pages_read": int(2 * wl.Hkv * (wl.ctx_lens // 16).sum()),
+            "acquire": int((d == 1).sum()), "compress": int((d == 2).sum())}
+
+
 # The oracle baseline spreads whole (sequence, KV head) groups over worker
 # processes; each worker builds the same seeded workload once and runs the
 # oracle unchanged on the groups it is handed.
@@ -304,6 +344,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the KV append (one token per sequence) on B8 and B64")
+    ap.add_argument("--decide", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the compress-or-acquire decision on B1, B8 Zipf and B64")
     ap.add_argument("--policy", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the split policy on short batches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -387,6 +429,10 @@ def main():
     if args.append:
         for name in ("b8_bimodal", "b64_prefix"):
             append[name] = time_append(name, 40, flush)
+    decide = {}
+    if args.decide:
+        for name in ("b1", "b8_zipf", "b64_prefix"):
+            decide[name] = time_decide(name, 40, flush)
 
     kv = head["kv_bytes"]
     achieved = kv / head["attn_ms_mean"] / 1e6
@@ -425,6 +471,8 @@ def main():
         result["split_policy"] = policy
     if append:
         result["kv_append"] = append
+    if decide:
+        result["budget_decide"] = decide
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result))

@@ -20,6 +20,8 @@
  *
  * Around the step: kvpage_append_kv is the step before it (append one token
  * per sequence, taking a page from a free list at a page boundary),
+ * kvpage_budget_decide turns the step's summary page maxima into GrowPage's
+ * compress-or-acquire decision,
  * kvpage_choose_split is a host-side policy that picks the split size for a
  * batch's context lengths, and kvpage_check_inputs reports violated
  * preconditions of the integer inputs (debug checks).
@@ -383,6 +385,50 @@ int kvpage_append_kv(const kvpage_shape* shape, const void* k_new, const void* v
                      void* k_pool, void* v_pool, int32_t* block_tables, const int32_t* ctx_lens,
                      int32_t* ctx_lens_out, const int32_t* free_pages, const int32_t* free_count,
                      int32_t* free_count_out, int32_t* status, hipStream_t stream);
+
+/* Decisions kvpage_budget_decide writes. */
+enum {
+  KVPAGE_DECIDE_NONE = 0,      /* not at a capacity boundary                      */
+  KVPAGE_DECIDE_ACQUIRE = 1,   /* take one more physical page                     */
+  KVPAGE_DECIDE_COMPRESS = 2   /* stay within the allocation; compress `victim`   */
+};
+
+/* GrowPage's budgeting decision (mlsanity.com entry, Abstract: the fast and
+ * slow query summaries' relative attention working sets estimate how demand
+ * evolves, and at each capacity boundary the system compresses KV within the
+ * current allocation or acquires another physical page when broader demand
+ * emerges; aitrending.vip article, Technical Details, on-demand page
+ * allocation).  The pages give no formula; this call computes, from the
+ * summary page maxima a budgeting decode step wrote:
+ *   working set of (summary k, sequence b, KV head g): with x_p =
+ *     page_max[k, b, g, p] for the sequence's pages p < ceil(ctx_b / P) and
+ *     page weights softmax(x), every page with x_p >= L, L the highest score
+ *     level whose pages scoring >= L hold at least tau of the weight (the
+ *     smallest top set covering tau; equal scores enter together).
+ *     ws_size[k, b, g] = its page count, ws_level[k, b, g] = L (+inf and 0
+ *     pages for an empty sequence);
+ *   F, S: the unions over KV heads of the fast (k = 0) and slow (k = 1) sets;
+ *     ws_union[0, b] = |F|, ws_union[1, b] = |S|;
+ *   decision[b]: KVPAGE_DECIDE_NONE unless ctx_b > 0 and ctx_b % P == 0 (the
+ *     last page is full: a capacity boundary); there KVPAGE_DECIDE_ACQUIRE
+ *     when |F| > |S| or every page lies in F or S, else
+ *     KVPAGE_DECIDE_COMPRESS with victim[b] = the page outside F and S whose
+ *     largest slow score over the KV heads is lowest (ties: the lowest page);
+ *     victim[b] = -1 otherwise.
+ * The weights are float32 exponentials summed exactly in 40-bit fixed point,
+ * so a set can differ from the exact one only where the exact covered
+ * fraction at its closing level lies within about 1e-5 of tau.
+ *   page_max: float32 [2, B, Hkv, max_pages], finite or -inf on each
+ *     sequence's pages (as the decode step writes it); ctx_lens: [B];
+ *   ws_size: int32 [2, B, Hkv]; ws_level: float32 [2, B, Hkv]; ws_union:
+ *     int32 [2, B]; decision, victim: int32 [B]; all device.
+ *   tau in (0, 1].
+ * shape: B, Hkv, page_size (16), max_pages (at most 2^23) are used; the
+ * other fields are checked as for the other calls.  Two kernels; negative
+ * kvpage_status on invalid arguments (nothing enqueued). */
+int kvpage_budget_decide(const kvpage_shape* shape, const float* page_max, const int32_t* ctx_lens,
+                         float tau, int32_t* ws_size, float* ws_level, int32_t* ws_union,
+                         int32_t* decision, int32_t* victim, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* kvpage_status_string(int status);

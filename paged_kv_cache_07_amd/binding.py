@@ -76,6 +76,7 @@ _SIGS = {
     "kvpage_choose_split": (ctypes.c_int32, [_S, _P, ctypes.c_int32]),
     "kvpage_append_kv": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "kvpage_check_inputs": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
+    "kvpage_budget_decide": (ctypes.c_int, [_S, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P]),
     "kvpage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -179,6 +180,18 @@ def kvpage_check_inputs(shape, ctx_lens, block_tables, tasks, group_offsets, n_t
     return _check("kvpage_check_inputs", lib().kvpage_check_inputs(
         ctypes.byref(shape), _ptr(ctx_lens), _ptr(block_tables), _ptr(tasks),
         _ptr(group_offsets), _ptr(n_tasks), int(capacity), _ptr(status), _stream(stream)))
+
+
+KVPAGE_DECIDE_NONE = 0
+KVPAGE_DECIDE_ACQUIRE = 1
+KVPAGE_DECIDE_COMPRESS = 2
+
+
+def kvpage_budget_decide(shape, page_max, ctx_lens, tau, ws_size, ws_level, ws_union, decision,
+                         victim, stream=None):
+    return _check("kvpage_budget_decide", lib().kvpage_budget_decide(
+        ctypes.byref(shape), _ptr(page_max), _ptr(ctx_lens), ctypes.c_float(tau), _ptr(ws_size),
+        _ptr(ws_level), _ptr(ws_union), _ptr(decision), _ptr(victim), _stream(stream)))
 
 
 def kvpage_workspace_bytes(shape: kvpage_shape, capacity: int) -> int:

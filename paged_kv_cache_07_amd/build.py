@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkvpage.so")
 C_ABI_CHECK = os.path.join(ROOT, "tests", "cabi", "kvpage_c_abi_check")
-SOURCES = ("api.hip", "queue.hip", "attn.hip", "merge.hip", "append.hip", "check.hip")
+SOURCES = ("api.hip", "queue.hip", "attn.hip", "merge.hip", "append.hip", "check.hip",
+           "decide.hip")
 ARCH = "gfx950"
 
 # The packed-FP32 feature is switched off: every float op stays scalar.

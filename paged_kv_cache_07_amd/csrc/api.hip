@@ -39,6 +39,9 @@ hipError_t launch_check_inputs(const kvpage_shape&, const int32_t*, const int32_
                                hipStream_t);
 hipError_t launch_page_mass(const kvpage_shape&, const kvpage_budget&, const void*, const float*,
                             const int32_t*, const int32_t*, int32_t, const void*, hipStream_t);
+hipError_t launch_budget_decide(const kvpage_shape&, const float*, const int32_t*, float, int32_t*,
+                                float*, int32_t*, int32_t*, int32_t*, hipStream_t);
+int decide_max_pages();
 
 namespace {
 
@@ -316,6 +319,21 @@ int kvpage_append_kv(const kvpage_shape* s, const void* k_new, const void* v_new
   return status_of(launch_append(*s, k_new, v_new, k_pool, v_pool, block_tables, ctx_lens,
                                  ctx_lens_out, free_pages, free_count, free_count_out, status,
                                  stream));
+}
+
+int kvpage_budget_decide(const kvpage_shape* s, const float* page_max, const int32_t* ctx_lens,
+                         float tau, int32_t* ws_size, float* ws_level, int32_t* ws_union,
+                         int32_t* decision, int32_t* victim, hipStream_t stream) {
+  KV_TRY(check_shape(s));
+  if (s->page_size != kPage) return KVPAGE_ERR_UNSUPPORTED;
+  if (s->max_pages > decide_max_pages()) return KVPAGE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * s->B * s->Hkv > INT32_MAX) return KVPAGE_ERR_UNSUPPORTED;
+  if (!(tau > 0.0f && tau <= 1.0f)) return KVPAGE_ERR_INVALID_ARG;
+  if (!page_max || !ctx_lens || !ws_size || !ws_level || !ws_union || !decision || !victim)
+    return KVPAGE_ERR_INVALID_ARG;
+  if (s->B == 0) return KVPAGE_OK;
+  return status_of(launch_budget_decide(*s, page_max, ctx_lens, tau, ws_size, ws_level, ws_union,
+                                        decision, victim, stream));
 }
 
 int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
