@@ -29,12 +29,24 @@
  * Problem statement and data layout (every tensor row-major, contiguous):
  *
  *   q            [B, Hq, d]                     f16 or bf16 (shape.dtype)
- *   k_pool       [num_pages, Hkv, P, d]         same dtype; P = page_size
- *   v_pool       [num_pages, Hkv, P, d]         same dtype
+ *   k_pool       [num_pages, Hkv, d/8, P, 8]    same dtype; P = page_size; each
+ *                                               (page, KV head) tile holds its
+ *                                               P keys as 16-byte chunks, chunk
+ *                                               c of every token together:
+ *                                               element (page, g, c, s, x) is
+ *                                               key element 8c + x of slot s
+ *   v_pool       [num_pages, Hkv, P, d]         same dtype, row-major tiles
  *   block_tables int32 [B, max_pages]           logical page -> physical page
  *   ctx_lens     int32 [B]                      tokens attended by sequence b
  *   out          [B, Hq, d]                     q's dtype, round to nearest even
  *   lse          float32 [B, Hq]                natural-log sum of exp(scores)
+ *
+ * The K tile order is the one vLLM's PagedAttention uses for its key cache
+ * (the head dimension split into 16-byte pieces outside the block's tokens):
+ * a load of four chunk rows of a tile is 1 KiB of contiguous memory that
+ * lands in the attention kernel's MFMA operand layout as it is, where a
+ * row-major key tile needs 64-byte pieces of 16 rows per load (measured 7%
+ * slower at one sequence of 32768 tokens, 8% on a batch of 8).
  *
  * Query head h reads KV head h / (Hq / Hkv).  Token t of sequence b is slot
  * t % P of physical page block_tables[b][t / P].  Scores are
@@ -272,14 +284,17 @@ int kvpage_page_mass(const kvpage_shape* shape, const kvpage_budget* budget, con
                      int32_t capacity, const void* workspace, hipStream_t stream);
 
 /* Test support (PersistentKV summary, Summary: native page tables): the pool
- * element offset each queued task reads for each of its tokens.  It is
+ * element offsets each queued task reads for each of its tokens.  They are
  * built from kvpage_split_attn's own addressing: the (page, KV head) tile
- * offset, then the row that the kernel's K and V lane maps load for the
- * token's slot, after checking that those lanes' pieces lie in that row and
- * cover its d elements exactly once (else -2).  The per-lane column split
- * inside a row is checked only by that coverage test and by the outputs.
- * offsets: int64 [capacity, split_tokens]; slot j of task i holds the offset
- * of token tok_begin + j, or -1 past tok_end.  Rows >= n_tasks untouched. */
+ * offset, then the place the kernel's K and V lane maps load for the
+ * token's slot, after checking that those lanes' pieces lie at that slot's
+ * places and cover its d elements exactly once (else -2).  Which lane holds
+ * which piece of a token is checked only by that coverage test and by the
+ * outputs.
+ * offsets: int64 [capacity, split_tokens, 2]; entry (i, j) holds, for token
+ * tok_begin + j of task i, the element offset of its first key element in
+ * k_pool ([0], chunk 0 of its slot) and of its value row in v_pool ([1]), or
+ * -1, -1 past tok_end.  Rows >= n_tasks untouched. */
 int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_tables,
                                 const kvpage_task* tasks, const int32_t* n_tasks,
                                 int32_t capacity, int64_t* offsets, hipStream_t stream);
@@ -368,7 +383,9 @@ enum {
  * A page id outside [0, num_pages) leaves b unchanged (a free-list entry it
  * came from is still used up; KVPAGE_APPEND_BAD_PAGE).  Then k_new[b, g, :]
  * and v_new[b, g, :] go to slot t % page_size of that page for every KV head
- * g, and ctx_lens_out[b] = t + 1 (t when b was left unchanged).
+ * g (in the pools' layouts: the key as d/8 chunks of the chunk-major tile,
+ * the value as one row), and ctx_lens_out[b] = t + 1 (t when b was left
+ * unchanged).
  *   k_new, v_new: [B, Hkv, d] in the pools' dtype, device.
  *   k_pool, v_pool, block_tables: updated in place, device.
  *   ctx_lens (read) and ctx_lens_out (written): [B] int32, device, must not

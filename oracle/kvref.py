@@ -12,9 +12,12 @@ What is computed, and where it comes from:
   split) tasks.  ``build_queue`` enumerates them in (sequence, KV head, split)
   order with fixed ``split_tokens``-token splits.
 * Page-table gather -- same page (Summary: native page tables; Method: work
-  mapped by KV-head group).  The K/V pool is ``[num_pages, Hkv, P, d]``
-  row-major; logical token ``t`` of sequence ``b`` lives in physical page
-  ``block_tables[b, t // P]`` at slot ``t % P``.
+  mapped by KV-head group).  Logical token ``t`` of sequence ``b`` lives in
+  physical page ``block_tables[b, t // P]`` at slot ``t % P``.  The V pool is
+  ``[num_pages, Hkv, P, d]`` (row-major tiles); the K pool is
+  ``[num_pages, Hkv, d/8, P, 8]``: each (page, KV head) tile keeps its keys as
+  16-byte chunks, chunk ``c`` of every slot together, so key element ``i``
+  of slot ``s`` is ``k_pool[page, g, i // 8, s, i % 8]``.
 * Attention -- grouped-query attention: query head ``h`` reads KV head
   ``h // (Hq // Hkv)``.  The oracle evaluates the plain softmax definition
   over the whole context (no splitting, no online softmax): split-KV with a
@@ -60,7 +63,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "widen", "build_queue", "gather_offsets", "logical_rows", "attention",
+    "widen", "build_queue", "gather_offsets", "logical_rows", "logical_key_rows", "attention",
     "update_summaries", "summary_page_max", "decode_step", "append_kv",
     "APPEND_FULL", "APPEND_NO_PAGE", "APPEND_BAD_PAGE",
     "check_inputs", "CHECK_LENGTH", "CHECK_PAGE", "CHECK_QUEUE",
@@ -114,30 +117,46 @@ def build_queue(ctx_lens, Hkv: int, split_tokens: int):
 
 
 def gather_offsets(block_tables, tasks, Hkv: int, page_size: int, d: int, split_tokens: int):
-    """Element offset into the K (or V) pool of every token a task reads.
+    """Element offsets into the K and V pools of every token a task reads.
 
-    Row ``i`` slot ``j`` is the offset of token ``tok_begin + j`` of task ``i``
-    (first element of its d-vector), or -1 when that token is past
-    ``tok_end``.  The pool is ``[num_pages, Hkv, P, d]`` row-major.
+    Entry ``[i, j]`` is, for token ``tok_begin + j`` of task ``i``, the
+    offset of its first key element in the K pool ``[num_pages, Hkv, d/8, P,
+    8]`` (``[..., 0]``) and of its value row in the V pool ``[num_pages, Hkv,
+    P, d]`` (``[..., 1]``); -1 when the token is past ``tok_end``.
     """
     n = len(tasks)
-    out = np.full((n, split_tokens), -1, dtype=np.int64)
+    out = np.full((n, split_tokens, 2), -1, dtype=np.int64)
     for i in range(n):
         b, g, t0, t1 = (int(v) for v in tasks[i])
         for j in range(t1 - t0):
             t = t0 + j
             page = int(block_tables[b, t // page_size])
-            out[i, j] = ((page * Hkv + g) * page_size + t % page_size) * d
+            tile = (page * Hkv + g) * page_size * d
+            out[i, j, 0] = tile + (t % page_size) * 8
+            out[i, j, 1] = tile + (t % page_size) * d
     return out
 
 
 def logical_rows(pool, block_tables, b: int, g: int, ctx: int, page_size: int, dtype: str):
-    """The ``ctx`` K (or V) rows of (sequence b, KV head g) in logical order, fp64."""
+    """The ``ctx`` V rows of (sequence b, KV head g) in logical order, fp64."""
     npages = -(-ctx // page_size)
     pages = np.asarray(block_tables[b, :npages], dtype=np.int64)
     tiles = pool[pages, g]                      # [npages, P, d], stored type
     d = tiles.shape[-1]
     return widen(tiles.reshape(npages * page_size, d)[:ctx], dtype)
+
+
+def logical_key_rows(k_pool, block_tables, b: int, g: int, ctx: int, page_size: int, dtype: str):
+    """The ``ctx`` K rows of (sequence b, KV head g) in logical order, fp64.
+
+    A K tile ``[d/8, P, 8]`` holds slot ``s``'s key as chunks ``[:, s, :]``.
+    """
+    npages = -(-ctx // page_size)
+    pages = np.asarray(block_tables[b, :npages], dtype=np.int64)
+    tiles = k_pool[pages, g]                    # [npages, d/8, P, 8], stored type
+    nch = tiles.shape[1]
+    rows = tiles.transpose(0, 2, 1, 3).reshape(npages * page_size, nch * 8)
+    return widen(rows[:ctx], dtype)
 
 
 def attention(q, k_pool, v_pool, block_tables, ctx_lens, page_size: int, scale: float,
@@ -169,7 +188,7 @@ def attention(q, k_pool, v_pool, block_tables, ctx_lens, page_size: int, scale: 
                 lse[b, h] = -np.inf
                 mass[b, h] = 0.0
             continue
-        K = logical_rows(k_pool, block_tables, b, g, ctx, page_size, dtype)
+        K = logical_key_rows(k_pool, block_tables, b, g, ctx, page_size, dtype)
         V = logical_rows(v_pool, block_tables, b, g, ctx, page_size, dtype)
         for h in heads:
             qh = widen(q[b, h], dtype)
@@ -219,7 +238,7 @@ def summary_page_max(s_next, k_pool, block_tables, ctx_lens, page_size: int, sca
         pm[:, b, g] = -np.inf
         if ctx == 0:
             continue
-        K = logical_rows(k_pool, block_tables, b, g, ctx, page_size, dtype)
+        K = logical_key_rows(k_pool, block_tables, b, g, ctx, page_size, dtype)
         for k in range(2):
             x = np.full(npages * page_size, -np.inf)
             x[:ctx] = scale * (K @ s_next[k, b, g])
@@ -268,7 +287,8 @@ def append_kv(k_pool, v_pool, block_tables, ctx_lens, k_new, v_new, free_pages, 
       ``APPEND_BAD_PAGE``.
 
     Then ``k_new[b, g]`` / ``v_new[b, g]`` are written to slot ``t % P`` of
-    that page for every KV head ``g``, and its length becomes ``t + 1``.
+    that page for every KV head ``g`` (the key as the slot's chunks of the K
+    tile), and its length becomes ``t + 1``.
 
     Returns new copies ``(k_pool, v_pool, block_tables, ctx_lens, free_count,
     status)``; inputs are not modified.  Pure integer and copy work: the
@@ -298,7 +318,8 @@ def append_kv(k_pool, v_pool, block_tables, ctx_lens, k_new, v_new, free_pages, 
             continue
         if new_page:
             bt[b, t // page_size] = page
-        k_pool[page, :, t % page_size, :] = k_new[b]
+        Hkv, nch = k_pool.shape[1], k_pool.shape[2]
+        k_pool[page, :, :, t % page_size, :] = np.asarray(k_new[b]).reshape(Hkv, nch, 8)
         v_pool[page, :, t % page_size, :] = v_new[b]
         ctx[b] = t + 1
     return k_pool, v_pool, bt, ctx, free_count - taken, status

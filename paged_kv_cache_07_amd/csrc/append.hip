@@ -85,13 +85,17 @@ __global__ void __launch_bounds__(kWave) append_kernel(const AppendParams p) {
   if (ok) {
     if (t % kPage == 0 && lane == 0) p.block_tables[(int64_t)b * p.max_pages + t / kPage] = page;
     const int n = p.Hkv * p.d;   // halves of one token, all KV heads
-    for (int x = 8 * lane; x < n; x += 8 * kWave) {
+    const int slot = t % kPage;
+    for (int x = 8 * lane; x < n; x += 8 * kWave) {   // one 16-byte chunk each
       const int g = x / p.d;
       const int i = x - g * p.d;
-      const int64_t dst = ((int64_t)(page * p.Hkv + g) * kPage + t % kPage) * p.d + i;
+      const int64_t tile = (int64_t)(page * p.Hkv + g) * kPage * p.d;
       const int64_t src = (int64_t)b * n + x;
-      *reinterpret_cast<uint4*>(p.k_pool + dst) = *reinterpret_cast<const uint4*>(p.k_new + src);
-      *reinterpret_cast<uint4*>(p.v_pool + dst) = *reinterpret_cast<const uint4*>(p.v_new + src);
+      // V rows are row-major in the tile, K chunk-major ([d/8][16][8]).
+      *reinterpret_cast<uint4*>(p.k_pool + tile + ((i / 8) * kPage + slot) * 8) =
+          *reinterpret_cast<const uint4*>(p.k_new + src);
+      *reinterpret_cast<uint4*>(p.v_pool + tile + slot * p.d + i) =
+          *reinterpret_cast<const uint4*>(p.v_new + src);
     }
   }
   if (lane == 0) p.ctx_out[b] = ok ? t + 1 : t;

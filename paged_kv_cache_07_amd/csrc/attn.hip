@@ -583,29 +583,63 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     const Rows rows_n = load_rows(nxt);
 
     // ---- pass 2: weights, page sums, P V into the run's accumulators ----
+    // Each V tile is first packed into its MFMA operands; its registers are
+    // then free, so the next tile is requested before this tile's MFMAs and
+    // the request does not wait behind them (with the request after the
+    // MFMAs, a wavefront's two-tile stream stalled on every V tile: ~15% of
+    // the B1 kernel time).
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int tau = PPT + i;
       const int slot = tau % DEPTH;
-      if (i < npg) {
+      const int nvalid = ntok - kPage * i;
+      if (i < npg && nvalid < kPage) {  // zero V rows past the context (they may hold NaN)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * r + e >= nvalid) {
+#pragma unroll
+            for (int w = 0; w < VW; ++w) buf[slot][VW * e + w] = 0u;
+          }
+      }
+      // Pages past the task's last one (the load count is fixed) contribute
+      // nothing: their operands are zero (their rows may hold anything), so
+      // the MFMAs below run unconditionally.  With them under a branch the
+      // accumulators were copied at the join after every tile, which waited
+      // for the MFMAs to finish and stalled the stream.
+      const bool used = i < npg;
+      u32x2 vop[VD];
+#pragma unroll
+      for (int j = 0; j < VD; ++j) {
+        const bool hi = j & 1;
+        const int w = j >> 1;
+        vop[j][0] = used ? pick_pair(buf[slot][w], buf[slot][VW + w], hi) : 0u;
+        vop[j][1] = used ? pick_pair(buf[slot][2 * VW + w], buf[slot][3 * VW + w], hi) : 0u;
+      }
+      if (tau + DEPTH < NT) {
+        load_tile(cur, ids, tau + DEPTH, buf[slot]);
+      } else {
+        // The next task's first K tiles; with no next task, the same number of
+        // loads re-read this task's last V tile (just fetched, so cached).
+        const int pg = max(has_next ? min(tau + DEPTH - NT, nxt.npg - 1) : npg - 1, 0);
+        const int32_t pid = clamp_page(__builtin_amdgcn_readlane(has_next ? ids_n : ids, pg), p.num_pages);
+        const char* base = (has_next ? kpool : vpool) + tile_offset(pid, has_next ? nxt.g : g, p.Hkv, D) * 2;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 w = tile_load<STREAM, u32x4>(base + koff[kb]);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) buf[slot][4 * kb + x] = w[x];
+        }
+      }
+      {
         const f32x4 sc = S[i * kWave + lane];
         float pe[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], p.c2, -mrun));
+        for (int e = 0; e < 4; ++e) pe[e] = used ? __builtin_amdgcn_exp2f(fmaf(sc[e], p.c2, -mrun)) : 0.f;
         const float psum = (pe[0] + pe[1]) + (pe[2] + pe[3]);
         l += psum;
         if constexpr (BUDGET) {
           const float page_sum = rows_sum(psum);
-          if (is_head && r == (i >> 2)) keep[i & 3] = page_sum;
-        }
-        const int nvalid = ntok - kPage * i;
-        if (nvalid < kPage) {  // zero V rows past the context (they may hold NaN)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * r + e >= nvalid) {
-#pragma unroll
-              for (int w = 0; w < VW; ++w) buf[slot][VW * e + w] = 0u;
-            }
+          if (used && is_head && r == (i >> 2)) keep[i & 3] = page_sum;
         }
         uint32_t pb[4];
 #pragma unroll
@@ -629,28 +663,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         }
 #pragma unroll
         for (int j = 0; j < VD; ++j) {
-          const bool hi = j & 1;
-          const int w = j >> 1;
-          u32x2 vop;
-          vop[0] = pick_pair(buf[slot][w], buf[slot][VW + w], hi);
-          vop[1] = pick_pair(buf[slot][2 * VW + w], buf[slot][3 * VW + w], hi);
-          O[j] = E::mfma_pv(pop, vop, O[j]);
-          if constexpr (BF) O[j] = E::mfma_pv(pop_lo, vop, O[j]);
-        }
-      }
-      if (tau + DEPTH < NT) {
-        load_tile(cur, ids, tau + DEPTH, buf[slot]);
-      } else {
-        // The next task's first K tiles; with no next task, the same number of
-        // loads re-read this task's last V tile (just fetched, so cached).
-        const int pg = max(has_next ? min(tau + DEPTH - NT, nxt.npg - 1) : npg - 1, 0);
-        const int32_t pid = clamp_page(__builtin_amdgcn_readlane(has_next ? ids_n : ids, pg), p.num_pages);
-        const char* base = (has_next ? kpool : vpool) + tile_offset(pid, has_next ? nxt.g : g, p.Hkv, D) * 2;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 w = tile_load<STREAM, u32x4>(base + koff[kb]);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) buf[slot][4 * kb + x] = w[x];
+          O[j] = E::mfma_pv(pop, vop[j], O[j]);
+          if constexpr (BF) O[j] = E::mfma_pv(pop_lo, vop[j], O[j]);
         }
       }
     }

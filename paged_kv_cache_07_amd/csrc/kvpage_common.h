@@ -1,9 +1,12 @@
 // Device-side helpers shared by the kvpage kernels (gfx950 / CDNA4).
 //
 // Addressing follows the paged layout of the PersistentKV summary
-// (aissential.tech, Summary: native page tables): the K and V pools are
-// [num_pages, Hkv, P, d] row-major, so one (page, KV head) tile of P tokens
-// is P*d contiguous elements.
+// (aissential.tech, Summary: native page tables): one (page, KV head) tile
+// of P tokens is P*d contiguous elements of the K pool and of the V pool.
+// Inside a tile, V is row-major [P][d]; K is chunk-major [d/8][P][8] (the
+// token's d elements as 16-byte chunks, chunk c of all P tokens together),
+// so that one 64-lane load of four chunk rows is 1 KiB of contiguous memory
+// and lands in the 16x16x32 MFMA operand layout as it is.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,14 +26,17 @@ __device__ __forceinline__ int64_t tile_offset(int32_t page, int32_t kv_head, in
 }
 
 // Lane maps of the attention kernel's tile loads (byte offsets inside one
-// (page, KV head) tile of D-element rows).  A wavefront's lane is (n, r) =
-// (lane % 16, lane / 16).
-//   K: for 16x16x32 MFMA block kb, lane (n, r) loads the 16 bytes of token n,
-//      elements 8 * (4 * kb + r) .. + 8: the MFMA's row operand (row = token).
+// (page, KV head) tile).  A wavefront's lane is (n, r) = (lane % 16, lane /
+// 16).
+//   K: for 16x16x32 MFMA block kb, lane (n, r) loads chunk 4 * kb + r (d
+//      elements 8 * (4 * kb + r) .. + 8) of token n: the MFMA's row operand
+//      (row = token); the 64 lanes read chunks 4kb .. 4kb+3 of all 16 tokens,
+//      1 KiB contiguous in the chunk-major K tile.
 //   V: for row group e, lane (n, r) loads token 4 * r + e, elements n * D / 16
 //      .. + D / 16: whole rows per 16 lanes.
 __host__ __device__ inline uint32_t k_piece_offset(int kb, int n, int r, int D) {
-  return (uint32_t)(n * D + 8 * (4 * kb + r)) * 2u;
+  (void)D;
+  return (uint32_t)(((4 * kb + r) * kPage + n) * 8) * 2u;
 }
 __host__ __device__ inline uint32_t v_piece_offset(int e, int n, int r, int D) {
   return (uint32_t)((4 * r + e) * D + n * (D / 16)) * 2u;

@@ -57,20 +57,21 @@ __global__ void __launch_bounds__(kWave) build_queue_kernel(
   }
 }
 
-// Row start (element offset inside a tile) that the attention kernel's lane
-// maps read for token slot s, or -1 unless the pieces its K lanes and its V
-// lanes load for that slot lie in row s and cover the row's d elements
-// exactly once each.
-__device__ int32_t lane_map_row(int s, int d) {
+// Offsets inside a tile of the first element of token slot s that the
+// attention kernel's lane maps read: K (chunk-major: s * 8) and V (row-major:
+// s * d).  Each is -1 unless the pieces the K lanes (lane (s, r), every MFMA
+// block) and the V lanes that land on slot s cover its d elements exactly
+// once each, at the layout's places.
+__device__ int2 lane_map_slot(int s, int d) {
   uint32_t kmask = 0, vmask = 0;
-  bool ok = true;
+  bool kok = true, vok = true;
   for (int kb = 0; kb < d / 32; ++kb)
     for (int r = 0; r < 4; ++r) {   // K: lane (s, r) holds token s of every MFMA block
-      const int el = (int)(k_piece_offset(kb, s, r, d) / 2);
-      const int col = el - s * d;
-      ok = ok && el / d == s && col % 8 == 0;
-      const uint32_t bit = 1u << ((col / 8) & 31);
-      ok = ok && !(kmask & bit);
+      const int el = (int)(k_piece_offset(kb, s, r, d) / 2) - s * 8;
+      const int c = el / (kPage * 8);   // chunk
+      kok = kok && el >= 0 && el % (kPage * 8) == 0 && c < d / 8;
+      const uint32_t bit = 1u << (c & 31);
+      kok = kok && !(kmask & bit);
       kmask |= bit;
     }
   for (int e = 0; e < 4; ++e)
@@ -79,20 +80,22 @@ __device__ int32_t lane_map_row(int s, int d) {
         const int el = (int)(v_piece_offset(e, n, r, d) / 2);
         if (el / d != s) continue;
         const int col = el - s * d;
-        ok = ok && col % (d / 16) == 0;
+        vok = vok && col % (d / 16) == 0;
         const uint32_t bit = 1u << ((col / (d / 16)) & 31);
-        ok = ok && !(vmask & bit);
+        vok = vok && !(vmask & bit);
         vmask |= bit;
       }
   const uint32_t full_k = (d / 8 >= 32) ? 0xffffffffu : ((1u << (d / 8)) - 1u);
-  ok = ok && kmask == full_k && vmask == 0xffffu;
-  return ok ? s * d : -1;
+  kok = kok && kmask == full_k;
+  vok = vok && vmask == 0xffffu;
+  return make_int2(kok ? s * 8 : -1, vok ? s * d : -1);
 }
 
 // One workgroup per queued task; lane j covers token slots j, j+64, ...  The
-// offset is built as the attention kernel builds its loads: the tile of the
-// token's page and KV head (tile_offset), then the row its lane maps read.
-// Slots whose lane maps fail the check above are written as -2.
+// offsets are built as the attention kernel builds its loads: the tile of
+// the token's page and KV head (tile_offset), then the place its lane maps
+// read for the token's slot.  Per token: [0] K, [1] V; -2 where the lane maps
+// fail the check above, -1 past tok_end.
 __global__ void __launch_bounds__(kWave) gather_offsets_kernel(
     const int32_t* __restrict__ block_tables, int32_t B, int32_t max_pages, int32_t Hkv, int32_t d,
     int32_t S, const kvpage_task* __restrict__ tasks, const int32_t* __restrict__ n_tasks,
@@ -106,12 +109,15 @@ __global__ void __launch_bounds__(kWave) gather_offsets_kernel(
     const int32_t* bt_row = block_tables + (int64_t)t.seq * max_pages;
     for (int j = threadIdx.x; j < S; j += kWave) {
       const int32_t tok = t.tok_begin + j;
-      int64_t off = -1;
+      int64_t ko = -1, vo = -1;
       if (tok < t.tok_end) {
-        const int32_t row = lane_map_row(tok % kPage, d);
-        off = row < 0 ? -2 : tile_offset(bt_row[tok / kPage], t.kv_head, Hkv, d) + row;
+        const int2 at = lane_map_slot(tok % kPage, d);
+        const int64_t tile = tile_offset(bt_row[tok / kPage], t.kv_head, Hkv, d);
+        ko = at.x < 0 ? -2 : tile + at.x;
+        vo = at.y < 0 ? -2 : tile + at.y;
       }
-      offsets[i * S + j] = off;
+      offsets[(i * S + j) * 2] = ko;
+      offsets[(i * S + j) * 2 + 1] = vo;
     }
   }
 }

@@ -165,7 +165,7 @@ class DecodeStep:
 
     def gather_offsets(self, stream=None):
         torch = _torch()
-        offs = torch.full((max(1, self.capacity), self.split_tokens), -7, dtype=torch.int64,
+        offs = torch.full((max(1, self.capacity), self.split_tokens, 2), -7, dtype=torch.int64,
                           device=self.device)
         K.kvpage_debug_gather_offsets(self.shape, self.block_tables, self.tasks, self.n_tasks,
                                       self.capacity, offs, stream)

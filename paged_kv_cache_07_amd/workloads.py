@@ -41,7 +41,8 @@ _CHUNK = 1 << 22
 
 __all__ = [
     "F16", "BF16", "Workload", "make", "NAMES", "f32_to_bf16_bits",
-    "poison_unused", "draw_queries", "kv_bytes", "custom",
+    "poison_unused", "draw_queries", "kv_bytes", "custom", "k_tiles_from_rows",
+    "k_rows_from_tiles",
 ]
 
 
@@ -68,7 +69,9 @@ def _nan_bits(dtype: str):
 class Workload:
     """One decode step's inputs.  Arrays are host numpy arrays.
 
-    ``q``: [B, Hq, d]; ``k_pool``/``v_pool``: [num_pages, Hkv, P, d]; float16
+    ``q``: [B, Hq, d]; ``k_pool``: [num_pages, Hkv, d/8, P, 8] (each tile's
+    keys as 16-byte chunks, chunk c of every slot together); ``v_pool``:
+    [num_pages, Hkv, P, d]; float16
     arrays for ``f16`` or uint16 bfloat16 bit patterns for ``bf16``.
     ``block_tables``: int32 [B, max_pages]; ``ctx_lens``: int32 [B].
     ``s_prev``: float32 [2, B, Hkv, d] query-summary state (fast, slow).
@@ -182,14 +185,14 @@ def _assemble(name, seed, rng, ctx, Hq, Hkv, d, P, S, dtype, num_pages,
     q32 = rng.standard_normal((B, Hq, d), dtype=np.float32)
     q = _store(q32, dtype)
     threads = threads or min(16, os.cpu_count() or 1)
-    shape = (num_pages, Hkv, P, d)
+    kshape, vshape = (num_pages, Hkv, d // 8, P, 8), (num_pages, Hkv, P, d)
     if fill_pools:
-        k_pool = _fill_pool(seed, 0, shape, dtype, threads)
-        v_pool = _fill_pool(seed, 1, shape, dtype, threads)
+        k_pool = _fill_pool(seed, 0, kshape, dtype, threads)
+        v_pool = _fill_pool(seed, 1, vshape, dtype, threads)
     else:  # lengths and tables only (queue-level checks): empty placeholder pools
-        empty = (0, Hkv, P, d)
-        k_pool = np.zeros(empty, dtype=np.float16 if dtype == F16 else np.uint16)
-        v_pool = k_pool.copy()
+        dt = np.float16 if dtype == F16 else np.uint16
+        k_pool = np.zeros((0, Hkv, d // 8, P, 8), dtype=dt)
+        v_pool = np.zeros((0, Hkv, P, d), dtype=dt)
     return Workload(
         name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, d=d, page_size=P, split_tokens=S,
         dtype=dtype, num_pages=num_pages, ctx_lens=ctx.astype(np.int32), block_tables=bt,
@@ -283,6 +286,20 @@ def custom(ctx, Hq, Hkv, d, page_size=16, split_tokens=256, dtype=F16, seed=7,
                      max_pages=max_pages, fill_pools=fill_pools)
 
 
+def k_tiles_from_rows(rows: np.ndarray) -> np.ndarray:
+    """K pool tiles from key rows: [..., P, d] -> [..., d/8, P, 8]."""
+    r = np.asarray(rows)
+    *lead, P, d = r.shape
+    return np.ascontiguousarray(np.swapaxes(r.reshape(*lead, P, d // 8, 8), -3, -2))
+
+
+def k_rows_from_tiles(tiles: np.ndarray) -> np.ndarray:
+    """Key rows from K pool tiles: [..., d/8, P, 8] -> [..., P, d]."""
+    t = np.asarray(tiles)
+    *lead, nch, P, _ = t.shape
+    return np.ascontiguousarray(np.swapaxes(t, -3, -2).reshape(*lead, P, nch * 8))
+
+
 def poison_unused(wl: Workload) -> Workload:
     """Copy of ``wl`` whose unreferenced pages and slots past each context are NaN."""
     k = wl.k_pool.copy()
@@ -298,6 +315,6 @@ def poison_unused(wl: Workload) -> Workload:
         if c % P:
             last = wl.block_tables[b, c // P]
             # A shared page is never a partial last page in these workloads.
-            k[last, :, c % P:, :] = nan
+            k[last, :, :, c % P:, :] = nan
             v[last, :, c % P:, :] = nan
     return dataclasses.replace(wl, k_pool=k, v_pool=v)

@@ -59,7 +59,7 @@ def test_append_golden_case():
     rng = np.random.default_rng(0)
     wl.block_tables = table
     wl.num_pages = 16
-    wl.k_pool = rng.standard_normal((16, 2, P, 64)).astype(np.float16)
+    wl.k_pool = rng.standard_normal((16, 2, 64 // 8, P, 8)).astype(np.float16)   # chunk-major tiles
     wl.v_pool = rng.standard_normal((16, 2, P, 64)).astype(np.float16)
     k_new, v_new = _new_rows(wl, rng)
     _, (_, _, bt, ctx, fc, st) = _check_append(wl, np.array([11, 12, 13, 14], np.int32)[:2],

@@ -124,7 +124,7 @@ def test_one_hot_query_returns_the_physical_address():
         for g in range(wl.Hkv):
             t = int(rng.integers(0, c))
             page = wl.block_tables[b, t // P]
-            k[page, g, t % P, g] = 8.0
+            k[page, g, g // 8, t % P, g % 8] = 8.0     # key element g of slot t % P
             q[b, g * wl.G:(g + 1) * wl.G, g] = 8.0 * np.sqrt(wl.d)
             want[b, g] = (page, g, t % P)
     wl2 = dataclasses.replace(wl, k_pool=k, v_pool=v, q=q)

@@ -78,7 +78,7 @@ def test_queue_closed_form_and_tiling(seed):
 # ------------------------------------------------------------- indexing ---
 
 def test_gather_offsets_decode_to_layout_coordinates():
-    wl = W.custom([37, 0, 100, 16, 1], Hq=6, Hkv=3, d=8, page_size=4, split_tokens=12, seed=3)
+    wl = W.custom([37, 0, 100, 16, 1], Hq=6, Hkv=3, d=16, page_size=4, split_tokens=12, seed=3)
     tasks, _, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
     offs = kvref.gather_offsets(wl.block_tables, tasks, wl.Hkv, wl.page_size, wl.d, wl.split_tokens)
     for i in range(n):
@@ -86,11 +86,13 @@ def test_gather_offsets_decode_to_layout_coordinates():
         for j in range(wl.split_tokens):
             t = t0 + j
             if t >= t1:
-                assert offs[i, j] == -1
+                assert np.all(offs[i, j] == -1)
                 continue
-            coords = np.unravel_index(offs[i, j], wl.k_pool.shape)
-            assert tuple(int(c) for c in coords) == (
-                int(wl.block_tables[b, t // wl.page_size]), int(g), int(t % wl.page_size), 0)
+            page, slot = int(wl.block_tables[b, t // wl.page_size]), int(t % wl.page_size)
+            kc = np.unravel_index(offs[i, j, 0], wl.k_pool.shape)     # [pages, Hkv, d/8, P, 8]
+            vc = np.unravel_index(offs[i, j, 1], wl.v_pool.shape)     # [pages, Hkv, P, d]
+            assert tuple(int(c) for c in kc) == (page, int(g), 0, slot, 0)
+            assert tuple(int(c) for c in vc) == (page, int(g), slot, 0)
 
 
 def test_attention_reads_the_tables_physical_rows():
@@ -107,7 +109,7 @@ def test_attention_reads_the_tables_physical_rows():
             t = int(rng.integers(0, c))
             k = np.zeros(wl.k_pool.shape, dtype=np.float16)
             page = wl.block_tables[b, t // P]
-            k[page, g, t % P, 0] = 8.0
+            k[page, g, 0, t % P, 0] = 8.0                 # key element 0 of slot t % P
             q = np.zeros(wl.q.shape, dtype=np.float16)
             q[b, :, 0] = 8.0 * math.sqrt(wl.d)          # scaled score 64 vs 0
             out, _, _ = kvref.attention(q, k, v, wl.block_tables, wl.ctx_lens, P, wl.scale, "f16")
@@ -122,7 +124,7 @@ def _identity_table_workload(ctx, Hq, Hkv, d, P, seed):
     B, mp = wl.block_tables.shape
     num_pages = B * mp + 1
     rng = np.random.default_rng(seed + 1)
-    k = rng.standard_normal((num_pages, Hkv, P, d)).astype(np.float16)
+    k = W.k_tiles_from_rows(rng.standard_normal((num_pages, Hkv, P, d)).astype(np.float16))
     v = rng.standard_normal((num_pages, Hkv, P, d)).astype(np.float16)
     bt = np.arange(B * mp, dtype=np.int32).reshape(B, mp)
     wl.k_pool, wl.v_pool, wl.block_tables, wl.num_pages = k, v, bt, num_pages
@@ -143,7 +145,7 @@ def test_attention_matches_torch_sdpa_on_contiguous_pages(Hq, Hkv):
     for b, c in enumerate(wl.ctx_lens):
         mask[b, 0, 0, :c] = True
     ref = torch.nn.functional.scaled_dot_product_attention(
-        torch.from_numpy(wl.q.astype(np.float64))[:, :, None, :], dense(wl.k_pool),
+        torch.from_numpy(wl.q.astype(np.float64))[:, :, None, :], dense(W.k_rows_from_tiles(wl.k_pool)),
         dense(wl.v_pool), attn_mask=mask, scale=wl.scale, enable_gqa=True)[:, :, 0, :].numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(mass.sum(axis=2), 1.0, rtol=0, atol=1e-12)
@@ -200,7 +202,8 @@ def test_constant_values_and_single_token_closed_forms():
         g = h // wl.G
         page = wl.block_tables[b, 0]
         assert np.array_equal(out[b, h], wl.v_pool[page, g, 0].astype(np.float64))
-        x0 = wl.scale * float(np.dot(wl.q[b, h].astype(np.float64), wl.k_pool[page, g, 0].astype(np.float64)))
+        krow = W.k_rows_from_tiles(wl.k_pool[page, g])[0]
+        x0 = wl.scale * float(np.dot(wl.q[b, h].astype(np.float64), krow.astype(np.float64)))
         assert abs(lse[b, h] - x0) < 1e-13
         assert mass[b, h, 0] == 1.0
 
@@ -240,7 +243,7 @@ def _brute(wl):
             g = h // G
             xs = []
             for t in range(c):
-                krow = wl.k_pool[wl.block_tables[b, t // P], g, t % P]
+                krow = wl.k_pool[wl.block_tables[b, t // P], g, :, t % P, :].reshape(-1)
                 xs.append(wl.scale * math.fsum(f(wl.q[b, h, i]) * f(krow[i]) for i in range(d)))
             M = max(xs)
             ws = [math.exp(x - M) for x in xs]
@@ -326,7 +329,7 @@ def test_page_max_matches_brute_force():
                     assert step["page_max"][k, b, 0, p] == -np.inf
                     continue
                 best = max(wl.scale * math.fsum(
-                    float(s[k, b, 0, i]) * float(wl.k_pool[wl.block_tables[b, t // P], 0, t % P, i])
+                    float(s[k, b, 0, i]) * float(wl.k_pool[wl.block_tables[b, t // P], 0, i // 8, t % P, i % 8])
                     for i in range(wl.d)) for t in toks)
                 assert abs(step["page_max"][k, b, 0, p] - best) < 1e-12
 
@@ -372,7 +375,7 @@ def test_append_golden_hand_worked():
     table = rows(kv["table"])
     ctx = ints(kv["ctx_in"])
     B = len(ctx)
-    k_pool = np.zeros((npages, Hkv, P, d), np.float16)
+    k_pool = np.zeros((npages, Hkv, d // 8, P, 8), np.float16)   # chunk-major key tiles
     v_pool = np.zeros((npages, Hkv, P, d), np.float16)
     k_new = (1 + np.arange(B * Hkv * d, dtype=np.float16).reshape(B, Hkv, d))
     v_new = -k_new
@@ -386,7 +389,9 @@ def test_append_golden_hand_worked():
     want_v = np.zeros_like(v_pool)
     for w in kv["written"]:
         b, page, slot = (int(x) for x in w.split(":"))
-        want_k[page, :, slot, :] = k_new[b]
+        for g in range(Hkv):
+            for i in range(d):                       # key element i: chunk i // 8, lane i % 8
+                want_k[page, g, i // 8, slot, i % 8] = k_new[b, g, i]
         want_v[page, :, slot, :] = v_new[b]
     assert np.array_equal(k2, want_k) and np.array_equal(v2, want_v)
     # inputs untouched
@@ -413,28 +418,32 @@ def test_append_then_gather_reads_the_new_token():
     assert np.array_equal(c2, wl.ctx_lens + 1)
     for b in range(wl.B):
         for g in range(wl.Hkv):
-            old = kvref.logical_rows(wl.k_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, "f16")
-            new = kvref.logical_rows(k2, bt2, b, g, int(c2[b]), 16, "f16")
+            old = kvref.logical_key_rows(wl.k_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, "f16")
+            new = kvref.logical_key_rows(k2, bt2, b, g, int(c2[b]), 16, "f16")
             assert np.array_equal(new[:-1], old) and np.array_equal(new[-1], k_new[b, g].astype(np.float64))
             newv = kvref.logical_rows(v2, bt2, b, g, int(c2[b]), 16, "f16")
             assert np.array_equal(newv[-1], v_new[b, g].astype(np.float64))
     # Only the appended slots changed in the pools.
-    changed = np.argwhere(np.any(k2 != wl.k_pool, axis=-1))
+    changed = np.argwhere(np.any(v2 != wl.v_pool, axis=-1))
     assert len(changed) <= wl.B * wl.Hkv
+    changed_k = np.argwhere(np.any(k2 != wl.k_pool, axis=(2, 4)))   # (page, head, slot)
+    assert len(changed_k) <= wl.B * wl.Hkv
 
 
 def test_append_bad_page_ids_change_nothing_for_that_sequence():
     kv, rows, ints = _read_append_golden()
     P = 16
-    k_pool = np.zeros((16, 1, P, 8), np.float16)
+    k_pool = np.zeros((16, 1, 1, P, 8), np.float16)            # d = 8: one chunk
+    v_pool = np.zeros((16, 1, P, 8), np.float16)
     table = np.array([[3, 15], [99, 15], [4, 15]], np.int32)   # row 1 points outside the pool
     ctx = np.array([5, 7, 16], np.int32)
     free = np.array([-1], np.int32)                             # seq 2 would take page -1
     k_new = np.ones((3, 1, 8), np.float16)
-    k2, _, t2, c2, fc2, st = kvref.append_kv(k_pool, k_pool, table, ctx, k_new, k_new, free, 1, P)
+    k2, v2, t2, c2, fc2, st = kvref.append_kv(k_pool, v_pool, table, ctx, k_new, k_new, free, 1, P)
     assert st == kvref.APPEND_BAD_PAGE
     assert np.array_equal(c2, [6, 7, 16]) and fc2 == 0 and np.array_equal(t2, table)
-    assert k2[3, 0, 5].all() and k2.sum() == 8
+    assert k2[3, 0, 0, 5].all() and k2.sum() == 8
+    assert v2[3, 0, 5].all() and v2.sum() == 8
 
 
 @pytest.mark.parametrize("split", [16, 32, 64, 256, 1 << 20])
@@ -451,7 +460,7 @@ def test_split_partials_merged_by_lse_equal_the_full_softmax(split):
     tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, split)
     parts = {}
     for b, g, t0, t1 in tasks:
-        K = kvref.logical_rows(wl.k_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, wl.dtype)[t0:t1]
+        K = kvref.logical_key_rows(wl.k_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, wl.dtype)[t0:t1]
         V = kvref.logical_rows(wl.v_pool, wl.block_tables, b, g, int(wl.ctx_lens[b]), 16, wl.dtype)[t0:t1]
         for h in range(g * wl.G, (g + 1) * wl.G):
             x = wl.scale * (K @ kvref.widen(wl.q[b, h], wl.dtype))
