@@ -521,15 +521,18 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int slot = i % DEPTH;
+      // The tile's operands are taken first and the slot refilled at once, so
+      // the next request does not wait behind this tile's MFMAs.
+      u32x4 a[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) a[kb][x] = buf[slot][4 * kb + x];
+      if (i + DEPTH < NT) load_tile(cur, ids, i + DEPTH, buf[slot]);
       if (i < npg) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          u32x4 a;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) a[x] = buf[slot][4 * kb + x];
-          acc = E::mfma_qk(a, qop[kb], acc);
-        }
+        for (int kb = 0; kb < KB; ++kb) acc = E::mfma_qk(a[kb], qop[kb], acc);
         if constexpr (BUDGET) {
           // Summary pieces sit in adjacent columns: add them into the lead column.
 #pragma unroll
@@ -555,7 +558,6 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           mloc = fmaxf(mloc, pm);
         }
       }
-      if (i + DEPTH < NT) load_tile(cur, ids, i + DEPTH, buf[slot]);
     }
     // The run's reference moves only when a task's max exceeds it by more
     // than 8 (log2 domain), so weights stay below 2^8 and rescales are rare.
