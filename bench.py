@@ -350,6 +350,8 @@ def main():
                     help="also time the split policy on short batches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--floor", action="store_true",
+                    help="only time a trivial kernel (a 4-byte fill) behind the same cache flush")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -372,6 +374,25 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4}))
+        return
+
+    if args.floor:
+        # What any kernel launched behind the 1 GiB flush costs when timed by
+        # HIP events around it, as the step is timed (kernel-trace durations
+        # of the same launches come from the profiler).
+        flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+        tiny = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(args.steps)]
+        for a, b in ev:
+            torch.sum(flush_buf, dim=0, out=sink[0])
+            a.record()
+            tiny.fill_(1)
+            b.record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_ms(b) for a, b in ev]) * 1e3
+        print(json.dumps({"floor_kernel": "4-byte fill behind the 1 GiB flush", "us_mean": float(us.mean()),
+                          "us_p50": float(np.median(us)), "launches": args.steps}))
         return
 
     flush = not args.warm
