@@ -407,6 +407,9 @@ def main():
             "kv_gbs_step": r["kv_bytes"] / r["step_ms_mean"] / 1e6,
             "kv_gbs_attn_kernel": r["kv_bytes"] / r["attn_ms_mean"] / 1e6,
             "frac_hbm_peak_attn": r["kv_bytes"] / r["attn_ms_mean"] / 1e6 / HBM_PEAK_GBS,
+            # Distinct pages only (a page shared by several sequences counted once):
+            # the bytes HBM has to deliver at least.
+            "frac_hbm_peak_attn_unique": r["kv_bytes_unique"] / r["attn_ms_mean"] / 1e6 / HBM_PEAK_GBS,
             "steps_per_s": 1e3 / r["step_ms_mean"],
             "step_ms_mean": r["step_ms_mean"], "attn_ms_mean": r["attn_ms_mean"],
             "kv_bytes": r["kv_bytes"], "kv_bytes_unique": r["kv_bytes_unique"],
