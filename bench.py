@@ -420,16 +420,16 @@ def main():
     # The split policy (kvpage_choose_split) beside the fixed 256-token split,
     # both in the same load mode: three short batches, where the fixed split
     # leaves wavefronts idle, with cached tile loads (streaming loads slow
-    # such a step by ~6%, which would flatter the policy); and the B8 bimodal
-    # lengths with streaming loads, where 256-token tasks end in a partial
-    # round.
+    # such a step by ~6%, which would flatter the policy); and the B8
+    # bimodal, B8 Zipf and B4 bimodal lengths with streaming loads, where the
+    # policy takes longer splits (fewer, longer tasks).
     policy = {}
     if args.policy:
         from paged_kv_cache_07_amd import binding as K
         from paged_kv_cache_07_amd import workloads as W
         cases = [(("custom", ctx), f"{len(ctx)}x{ctx[0]}", False)
                  for ctx in ([8192], [4096] * 4, [16384])]
-        cases.append((("named", "b8_bimodal"), "b8_bimodal", True))
+        cases += [(("named", n), n, True) for n in ("b8_bimodal", "b8_zipf", "b4_bimodal")]
         for spec, label, stream_kv in cases:
             if spec[0] == "custom":
                 wl = W.custom(spec[1], Hq=32, Hkv=8, d=128, seed=21, fill_pools=False)

@@ -125,7 +125,8 @@ typedef struct {
 #define KVPAGE_FLAG_STREAM_KV 1u
 
 /* Problem shape.  Supported by the kernels: page_size == 16; d in {64, 128};
- * 1 <= Hq / Hkv <= 8; split_tokens a multiple of page_size in [16, 256];
+ * 1 <= Hq / Hkv <= 8; split_tokens a multiple of page_size in [16, 256]
+ * or a multiple of 256 in [512, 4096] (run as consecutive 16-page pieces);
  * dtype f16 or bf16; scale finite and > 0.  flags: 0 or
  * KVPAGE_FLAG_STREAM_KV (any other bit is KVPAGE_ERR_INVALID_ARG). */
 typedef struct {
@@ -301,21 +302,27 @@ int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_
 
 /* Split size for one decode step, chosen per workload (PersistentKV
  * summary, Summary: its throughput gains come from a policy that picks the
- * decode configuration for each workload).  Among the splits S in
- * {256, 128, 64, 32, 16} tokens whose queue holds at least one task per
- * resident wavefront of the attention kernel (n = Hkv * sum_b ceil(ctx_b / S)
- * >= wavefronts), returns the one whose busiest wavefront has the least work
- * under the kernel's schedule: with rounds = ceil(n / (16 * wavefronts)) and
- * c = ceil(n / (rounds * wavefronts)) tasks per chunk, c * rounds tasks of
- * S / 16 pages each plus a fixed cost per task (measured: half a page with
- * KVPAGE_FLAG_STREAM_KV in shape.flags, one and a half without); ties go to
- * the longer split.  The page size (16) if no split fills the wavefronts,
- * 256 if every context is empty.  A queue shorter than the resident
- * wavefronts leaves the GPU partly idle; one that ends in a partial round
- * leaves a tail (6656 tasks of 256 tokens on 1024 wavefronts: 7 per
- * wavefront where 6.5 would do; with streaming loads split 128 gives 13 per
- * wavefront and ran 3.5% faster).  The kernel instance for short splits
- * issues loads for only the pages a split can hold.
+ * decode configuration for each workload).  Candidates: S in {4096, 2048,
+ * ..., 32, 16} tokens with KVPAGE_FLAG_STREAM_KV in shape.flags, {256, ...,
+ * 16} without (pages that may be shared are then read by wavefronts running
+ * side by side close together in time, from cache: on a batch sharing a
+ * prefix, 256 ran 1.7% faster than 1024).  Only splits whose queue holds at
+ * least one task per resident wavefront of the attention kernel
+ * (n = Hkv * sum_b ceil(ctx_b / S) >= wavefronts) qualify.  Under the
+ * kernel's schedule the busiest wavefront takes c * rounds positions, with
+ * rounds = ceil(n / (m * wavefronts)), c = ceil(n / (rounds * wavefronts))
+ * and m = 16 / ceil(S / 256) positions per chunk at most, each of at most
+ * S / 16 pages.  Cost in pages: max(P / wavefronts, busiest pages / 1.5) +
+ * f * c * rounds, where P = Hkv * sum_b ceil(ctx_b / 16) is the step's
+ * pages (the kernel is bound by HBM, and a wavefront streams 1.5-1.8x
+ * faster once the others have finished) and f the fixed cost of a position
+ * (measured: half a page with streaming loads, one and a half cached).
+ * Returns the cheapest, ties to the longer split; the page size (16) if no
+ * split fills the wavefronts, 256 if every context is empty.  Measured on
+ * MI355X against 256: 4 long + 4 short sequences 1024 (2.3% faster
+ * attention), Zipf lengths 2048 (4.1%), 4 bimodal sequences 1024 (2.8%);
+ * one 32768-token sequence keeps 256 (512 leaves half the wavefronts idle:
+ * 26% slower).
  *   shape: B, Hq, Hkv, d, page_size, max_pages, num_pages, dtype, scale and
  *     flags as for the other calls (flags as the step will use them);
  *     split_tokens is ignored.

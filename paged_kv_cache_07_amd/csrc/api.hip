@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "kvpage_common.h"
@@ -28,7 +29,7 @@ hipError_t launch_append(const kvpage_shape&, const void*, const void*, void*, v
                          const int32_t*, int32_t*, const int32_t*, const int32_t*, int32_t*,
                          int32_t*, hipStream_t);
 int split_attn_waves_per_cu();
-int split_attn_chunk_max();
+int split_attn_chunk_max(int split_tokens);
 hipError_t launch_merge(const kvpage_shape&, const int32_t*, int32_t, const void*, void*, float*,
                         hipStream_t);
 hipError_t launch_merge_finish(const kvpage_shape&, const kvpage_budget&, const void*,
@@ -69,7 +70,11 @@ int check_supported(const kvpage_shape* s) {
   if (s->d != 64 && s->d != 128) return KVPAGE_ERR_UNSUPPORTED;
   const int G = s->Hq / s->Hkv;
   if (G < 1 || G > 8) return KVPAGE_ERR_UNSUPPORTED;
-  if (s->split_tokens > 16 * kPage) return KVPAGE_ERR_UNSUPPORTED;
+  // Splits up to 16 pages, or whole multiples of 16 pages up to 256 pages
+  // (run as pieces of 16 pages).
+  if (s->split_tokens > 16 * kPage &&
+      (s->split_tokens % (16 * kPage) != 0 || s->split_tokens > 256 * kPage))
+    return KVPAGE_ERR_UNSUPPORTED;
   if ((int64_t)s->B * s->Hq > INT32_MAX) return KVPAGE_ERR_UNSUPPORTED;
   return KVPAGE_OK;
 }
@@ -359,17 +364,28 @@ int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
       return KVPAGE_ERR_HIP;
     waves = (int64_t)cus * split_attn_waves_per_cu();
   }
-  const int32_t longest = 16 * t.page_size;
-  if (total == 0) return longest;
-  // Among the splits whose queue holds a task for every resident wavefront,
-  // the one whose busiest wavefront has the least work under the attention
-  // kernel's schedule (rounds of chunks of at most chunk_max positions):
-  // its tasks times (pages per task + a task's fixed cost), the fixed cost
-  // measured at half a page with streaming tile loads and one and a half
-  // with cached ones.  Ties go to the longer split; none qualifies: the page
-  // size.
-  const int64_t chunk_max = split_attn_chunk_max();
-  const int64_t task_cost2 = (t.flags & KVPAGE_FLAG_STREAM_KV) ? 1 : 3;   // twice the fixed cost
+  if (total == 0) return 16 * t.page_size;
+  // Every candidate split from the longest the kernel runs down to the page
+  // size is priced by the busiest wavefront under the attention kernel's
+  // schedule (rounds of chunks of at most chunk_max positions): n queue
+  // positions of at most `split` tokens each.  The kernel is bound by HBM, so
+  // the cost is the larger of the mean pages per wavefront (the same for
+  // every split) and the busiest wavefront's pages over 1.5: a wavefront
+  // streams 1.5-1.8x faster once the others have finished (measured on
+  // MI355X: 16 pages per wavefront over 1024 of them, 0.77 pages/us each; 64
+  // over 256, 1.37).  Each position adds a fixed cost, measured at half a page
+  // with streaming loads and one and a half with cached ones.  Only splits
+  // with a task for every resident wavefront qualify; ties go to the longer
+  // split; none qualifies: the page size.  Where pages may be shared (cached
+  // loads) splits stay at 16 pages or less: wavefronts running side by side
+  // then read a shared prefix's pages close together in time, from L2 (B64
+  // with a shared prefix: 256 tokens 1.7% faster than 1024).
+  const bool streaming = (t.flags & KVPAGE_FLAG_STREAM_KV) != 0;
+  const int32_t longest = (streaming ? 256 : 16) * t.page_size;
+  int64_t total_pages = 0;
+  for (int b = 0; b < t.B; ++b) total_pages += (ctx_lens_host[b] + t.page_size - 1) / t.page_size;
+  total_pages *= t.Hkv;
+  const int64_t fixed6 = streaming ? 3 : 9;   // six times the fixed cost per position
   int32_t best = 0;
   int64_t best_cost = INT64_MAX;
   for (int32_t split = longest; split >= t.page_size; split /= 2) {
@@ -377,9 +393,13 @@ int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
     for (int b = 0; b < t.B; ++b) tasks += (ctx_lens_host[b] + split - 1) / split;
     tasks *= t.Hkv;
     if (tasks < waves) continue;
+    const int64_t chunk_max = split_attn_chunk_max(split);
     const int64_t rounds = (tasks + waves * chunk_max - 1) / (waves * chunk_max);
     const int64_t c = (tasks + waves * rounds - 1) / (waves * rounds);
-    const int64_t cost = c * rounds * (2 * (split / t.page_size) + task_cost2);   // twice the work
+    const int64_t n = c * rounds;                          // positions on the busiest wavefront
+    const int64_t busiest = n * (split / t.page_size);     // its pages, at most
+    // Six times `waves` times the cost in pages.
+    const int64_t cost = std::max(6 * total_pages, 4 * waves * busiest) + fixed6 * waves * n;
     if (cost < best_cost) {
       best_cost = cost;
       best = split;

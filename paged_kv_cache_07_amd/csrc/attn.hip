@@ -119,7 +119,7 @@ struct AttnParams {
 
 constexpr int kWavesPerGroup = 4;
 constexpr int kMaxPagesPerTask = 16;   // pages of the longest split (256 tokens)
-constexpr int kRunMax = 16;   // most queue positions one wavefront takes in a row
+constexpr int kRunMax = 16;   // most pieces of work one wavefront takes in a row
 
 // All-reduce over the four 16-lane rows of a wavefront (lanes n, n+16, n+32,
 // n+48) with the gfx950 row-swap permutes: after a swap each lane holds its
@@ -215,8 +215,9 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   constexpr int VW = VD / 2;   // V dwords per lane per token
   constexpr int TW = D / 8;    // dwords per lane per tile (K or V)
   constexpr int NPC = E::kPieces;
-  // PPT: pages per task this instance handles (the split is at most PPT
-  // pages); every task issues loads for exactly PPT K and PPT V tiles.
+  // PPT: pages per piece this instance handles (a split of at most PPT
+  // pages is one piece, a longer one several); every piece issues loads for
+  // exactly PPT K and PPT V tiles.
   static_assert(PPT <= kMaxPagesPerTask, "at most 16 pages per task");
   constexpr int NT = 2 * PPT;
   // The next task's first tiles are fetched into the slots its first pages
@@ -265,8 +266,22 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   const char* kpool = reinterpret_cast<const char*>(p.k_pool);
   const char* vpool = reinterpret_cast<const char*>(p.v_pool);
 
+  // A unit of work: piece `piece` (at most PPT pages) of queue entry t.
+  // A split longer than PPT pages is run as consecutive pieces of one task;
+  // tb0 / te are the task's token range, tok_begin / tok_end the piece's.
   struct Task {
-    int t, b, g, tok_begin, tok_end, ntok, npg, lp0;
+    int t, b, g, tok_begin, tok_end, ntok, npg, lp0, piece, tb0, te;
+    bool last;   // the task's last piece
+  };
+  auto unit = [&](Task k, int pc) {
+    k.piece = pc;
+    k.tok_begin = k.tb0 + pc * (PPT * kPage);
+    k.tok_end = min(k.te, k.tok_begin + PPT * kPage);
+    k.ntok = k.tok_end - k.tok_begin;
+    k.npg = (k.ntok + kPage - 1) / kPage;
+    k.lp0 = k.tok_begin / kPage;
+    k.last = k.tok_end >= k.te;
+    return k;
   };
   SeqScan sq = {0, 0, 0, 0, 0};
   // Queue entry t: read from the queue, or (fused build) derived from the lengths.
@@ -304,12 +319,9 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     k.t = t;
     k.b = tk.seq;
     k.g = tk.kv_head;
-    k.tok_begin = tk.tok_begin;
-    k.tok_end = tk.tok_end;
-    k.ntok = tk.tok_end - tk.tok_begin;
-    k.npg = (k.ntok + kPage - 1) / kPage;
-    k.lp0 = tk.tok_begin / kPage;
-    return k;
+    k.tb0 = tk.tok_begin;
+    k.te = tk.tok_end;
+    return unit(k, 0);
   };
   // Lane i < npg holds the physical id of the task's page i.
   auto load_page_ids = [&](const Task& k) -> int32_t {
@@ -473,14 +485,17 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   } else {
     ntask = min(p.n_tasks[0], p.capacity);
   }
-  // The queue is cut into chunks of c consecutive positions (c <= kRunMax,
-  // sized so every wavefront gets nearly the same number of chunks); wave gw
-  // runs chunks gw, gw + nwaves, ...  Run partials start at multiples of c.
+  // The queue is cut into chunks of c consecutive positions (c pieces of
+  // work at most kRunMax, sized so every wavefront gets nearly the same
+  // number of chunks); wave gw runs chunks gw, gw + nwaves, ...  Run
+  // partials start at multiples of c.
+  const int pieces = (p.split_tokens + PPT * kPage - 1) / (PPT * kPage);   // per task
+  const int cmax = kRunMax / pieces;
   int c;
-  if (ntask <= nwaves * kRunMax) {   // one round
+  if (ntask <= nwaves * cmax) {   // one round
     c = max(1, (int)div_by((uint32_t)(ntask + nwaves - 1), p.div_waves));
   } else {
-    const int rounds = (ntask + nwaves * kRunMax - 1) / (nwaves * kRunMax);
+    const int rounds = (ntask + nwaves * cmax - 1) / (nwaves * cmax);
     c = (ntask + nwaves * rounds - 1) / (nwaves * rounds);
   }
   if (blockIdx.x == 0 && wave == 0 && lane == 0) p.ws_hdr[0] = c;
@@ -502,10 +517,11 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   int run_start = t_first;
   int run_lp0 = cur.lp0;
   int run_pages = 0;
-  // A run is consecutive tasks of one (sequence, KV head); all but its last
-  // are whole splits of pps pages, so page pp of the run is page pp % pps of
-  // its task pp / pps.
-  const int pps = p.split_tokens / kPage;
+  int run_units = 0;   // pieces of the run done so far
+  // A run is consecutive pieces of consecutive tasks of one (sequence, KV
+  // head); all but its last are whole pieces of upg pages, so page pp of the
+  // run is page pp % upg of its piece pp / upg.
+  const int upg = min(p.split_tokens / kPage, PPT);
   float mrun = is_head ? -INFINITY : INFINITY;   // log2-domain reference; non-head lanes weigh 0
   float l = 0.f;
   f32x4 O[VD];
@@ -575,12 +591,15 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       }
     }
 
-    // ---- the next task of this wave (or this one again at the end) ----
-    const bool in_chunk = cur.t + 1 < chunk_end;
+    // ---- the next piece of this wave (or this one again at the end) ----
+    const bool more = !cur.last;   // another piece of this task
+    const bool in_chunk = more || cur.t + 1 < chunk_end;
     const bool next_chunk = !in_chunk && (chunk + nwaves) * c < ntask;
     const bool has_next = in_chunk || next_chunk;
-    const int tn = in_chunk ? cur.t + 1 : (next_chunk ? (chunk + nwaves) * c : cur.t);
-    const Task nxt = fetch(tn);
+    const int tn = more ? cur.t
+                        : (cur.t + 1 < chunk_end ? cur.t + 1
+                                                 : (next_chunk ? (chunk + nwaves) * c : cur.t));
+    const Task nxt = more ? unit(cur, cur.piece + 1) : fetch(tn);
     const int32_t ids_n = load_page_ids(nxt);
     const Rows rows_n = load_rows(nxt);
 
@@ -671,16 +690,17 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       }
     }
 
-    // ---- per task: stage the queue entry and budgeting values in LDS ----
-    const int kin = cur.t - run_start;   // position inside the run, < kRunMax
+    // ---- per piece: stage the queue entry and budgeting values in LDS ----
+    const int kin = run_units;            // piece position inside the run, < kRunMax
+    const int ktask = cur.t - run_start;  // task position inside the run
     if constexpr (FUSEDQ) {
-      if (lane == 0) {
+      if (lane == 0 && cur.piece == 0) {
         kvpage_task out_t;
         out_t.seq = b;
         out_t.kv_head = g;
-        out_t.tok_begin = cur.tok_begin;
-        out_t.tok_end = cur.tok_end;
-        lds_task[wave][kin] = out_t;
+        out_t.tok_begin = cur.tb0;
+        out_t.tok_end = cur.te;
+        lds_task[wave][ktask] = out_t;
       }
     }
     if constexpr (BUDGET) {
@@ -690,6 +710,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       if (r == 0 && is_head) lds_tref[wave][kin][n] = mrun;
     }
     run_pages += npg;
+    ++run_units;
 
     // ---- run boundary: write the run's partial (m, l, o) per head ----
     const bool new_group = nxt.b != b || nxt.g != g;
@@ -708,7 +729,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           for (int j = 0; j < VD; ++j) dst[j] = O[j][e];
         }
       }
-      const int nk = kin + 1;
+      const int nk = ktask + 1;
       if constexpr (FUSEDQ) {
         __builtin_amdgcn_wave_barrier();
         if (lane < nk) p.tasks_out[run_start + lane] = lds_task[wave][lane];
@@ -740,16 +761,16 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mrun), h));
           float* row = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0;
           for (int pp = lane; pp < rp; pp += kWave) {
-            const int kk = pp / pps;   // task of the run holding page pp
-            row[pp] = lds_mass[wave][kk][h][pp - kk * pps] *
+            const int kk = pp / upg;   // piece of the run holding page pp
+            row[pp] = lds_mass[wave][kk][h][pp - kk * upg] *
                       __builtin_amdgcn_exp2f(lds_tref[wave][kk][h] - mh);
           }
         }
         for (int which = 0; which < 2; ++which) {
           float* row = p.page_max + (((int64_t)which * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0;
           for (int pp = lane; pp < rp; pp += kWave) {
-            const int kk = pp / pps;
-            row[pp] = lds_pmax[wave][kk][which][pp - kk * pps];
+            const int kk = pp / upg;
+            row[pp] = lds_pmax[wave][kk][which][pp - kk * upg];
           }
         }
       }
@@ -761,6 +782,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       run_start = tn;
       run_lp0 = nxt.lp0;
       run_pages = 0;
+      run_units = 0;
       mrun = is_head ? -INFINITY : INFINITY;
       l = 0.f;
 #pragma unroll
@@ -841,7 +863,8 @@ static hipError_t dispatch_ppt(const kvpage_shape& s, const AttnParams& p, int c
 
 // The instance with the fewest pages per task that holds one split: a task
 // issues loads for all of its instance's pages, so a short split run by the
-// 16-page instance would spend most of its loads on repeats.
+// 16-page instance would spend most of its loads on repeats.  Splits longer
+// than 16 pages run on the 16-page instance as consecutive pieces.
 template <bool FUSEDQ, bool STREAM>
 static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
@@ -855,8 +878,10 @@ static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capac
 // Wavefronts of one resident round per compute unit (one workgroup per CU).
 int split_attn_waves_per_cu() { return kWavesPerGroup; }
 
-// Most queue positions in one chunk of the schedule.
-int split_attn_chunk_max() { return kRunMax; }
+// Most queue positions in one chunk of the schedule at this split.
+int split_attn_chunk_max(int split_tokens) {
+  return kRunMax / ((split_tokens + 16 * kPage - 1) / (16 * kPage));
+}
 
 // Fused queue build: B <= 64 sequences (one lane each in the task lookup).
 bool split_attn_can_fuse_queue(const kvpage_shape& s) { return s.B >= 1 && s.B <= kWave; }

@@ -74,7 +74,10 @@ def test_invalid_shapes_are_rejected(kw, status):
 
 
 @pytest.mark.parametrize("kw", [dict(d=96), dict(page_size=8, split_tokens=256),
-                                dict(Hq=80, Hkv=8), dict(split_tokens=512)])
+                                dict(Hq=80, Hkv=8),
+                                # past 16 pages only whole multiples of 16 pages, up to 256
+                                dict(split_tokens=272), dict(split_tokens=768 + 16),
+                                dict(split_tokens=8192)])
 def test_unsupported_shapes_report_unsupported(kw):
     s = _shape(**kw)
     cap = K.kvpage_queue_capacity(s)
@@ -129,9 +132,11 @@ def test_status_strings():
 
 def test_choose_split_fills_the_resident_wavefronts():
     """Among the splits whose queue has a task per resident wavefront
-    (Hkv * sum ceil(ctx / S) >= W), the least work on the busiest wavefront;
-    the page size if none qualifies, the longest split for an all-empty
-    batch.  Pure host arithmetic with W given (cases worked by hand)."""
+    (Hkv * sum ceil(ctx / S) >= W), the least cost: the larger of the mean
+    pages per wavefront and the busiest wavefront's pages over 1.5, plus a
+    fixed cost per position; the page size if none qualifies, 256 for an
+    all-empty batch.  Pure host arithmetic with W given (cases worked by
+    hand)."""
     def pick(ctx, W=1024, **kw):
         return K.kvpage_choose_split(_shape(B=len(ctx), **kw), ctx, W)
     assert pick([32768]) == 256          # 8 * 128 tasks = 1024
@@ -148,24 +153,35 @@ def test_choose_split_fills_the_resident_wavefronts():
     assert pick([16384], Hq=16, Hkv=4) == 64   # half the KV heads, half the tasks
     for S in (16, 32, 64, 128, 256):
         assert pick([8192] * 3, W=3 * 8 * 8192 // S) >= S
-    # A partial last round: 4 x 208 splits of 256 per KV head = 6656 tasks,
-    # 7 per wavefront; at 128, 13312 tasks, 13 each.  In pages plus the fixed
-    # cost per task: streaming loads (1/2 page) 7 * 16.5 = 115.5 against
-    # 13 * 8.5 = 110.5, so 128; cached loads (3/2) 122.5 against 123.5, 256.
+    # Four sequences of 53248 tokens (13312 pages over 1024 wavefronts: 104
+    # each).  Streaming: 4096 and 2048 leave wavefronts idle (416, 832
+    # tasks); 1024 gives 1664 tasks, two 64-page positions on the busiest
+    # wavefront: max(104, 128 / 1.5) + 2 * 1/2 = 105, against 512 (four
+    # positions: 106), 256 (seven: 107.5).  Cached: at most 256, whose seven
+    # positions cost 104 + 7 * 3/2 = 114.5 against 128's thirteen (123.5).
     stream = K.KVPAGE_FLAG_STREAM_KV
-    assert pick([53248] * 4, max_pages=8192, flags=stream) == 128
+    assert pick([53248] * 4, max_pages=8192, flags=stream) == 1024
     assert pick([53248] * 4, max_pages=8192) == 256
-    # 9216 tasks, 9 each (148.5); at 128, 18432 in two rounds of 9 (153).
-    assert pick([73728] * 4, max_pages=8192, flags=stream) == 256
+    # 73728 tokens each (144 pages per wavefront): 2048 gives 1152 tasks, two
+    # 128-page positions (max(144, 256 / 1.5) + 1 = 171.7); 1024 three of 64
+    # (144 + 1.5); 512 five of 32 (146.5).
+    assert pick([73728] * 4, max_pages=8192, flags=stream) == 1024
+    # Chunks of 4096-token tasks hold one position: 8 sequences of 262144
+    # tokens on 2048 wavefronts (512 pages each) give 4096 tasks of 4096, two
+    # rounds of one position (512 + 2 * 1/2); 2048 two rounds of two
+    # (512 + 2), 1024 two of four (512 + 4).
+    assert pick([2097152 // 8] * 8, max_pages=16384, flags=stream, W=2048) == 4096
 
 
 def test_choose_split_on_the_reference_workloads():
     """With the load mode the benchmark uses (streaming unless pages are
-    shared), B8 bimodal (6656 tasks of 256: 7 per wavefront where 6.5 would
-    do) takes 128, measured 3.5% faster; the others keep 256, as measured."""
+    shared), as measured on MI355X against 256-token splits: B8 bimodal and
+    B4 bimodal take 1024 (2.3% and 2.8% faster attention), Zipf lengths 2048
+    (4.1%), B8 uniform 1024 (no difference measured); one long sequence and
+    the shared-prefix batch keep 256."""
     from paged_kv_cache_07_amd import workloads as W
-    want = {"b1": 256, "b8_bimodal": 128, "b8_uniform": 256, "b8_zipf": 256, "b4_bimodal": 256,
-            "b64_prefix": 256}
+    want = {"b1": 256, "b8_bimodal": 1024, "b8_uniform": 1024, "b8_zipf": 2048,
+            "b4_bimodal": 1024, "b64_prefix": 256}
     for name, split in want.items():
         wl = W.make(name, fill_pools=False)
         flags = 0 if wl.shares_pages() else K.KVPAGE_FLAG_STREAM_KV

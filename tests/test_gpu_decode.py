@@ -154,11 +154,13 @@ def test_oracle_sized_configs_all_outputs(name, div):
 
 @pytest.mark.parametrize("name,split", [("b1", 256), ("b8_bimodal", 256), ("b8_uniform", 256),
                                         ("b8_zipf", 256), ("b64_prefix", 256), ("b4_bimodal", 256),
-                                        ("b8_bimodal", 128)])
+                                        ("b8_bimodal", 1024), ("b8_zipf", 2048),
+                                        ("b4_bimodal", 1024), ("b8_uniform", 1024)])
 def test_full_size_sampled_rows(name, split):
     """Full-size workloads in the launch configurations bench.py times (one
     kvpage_decode_step call, streaming tile loads unless pages are shared;
-    B8 bimodal also at the split the policy picks for it): one query head of
+    the B8 and B4 workloads also at the splits the policy picks for them,
+    run as 16-page pieces): one query head of
     every (sequence, KV head) group, plus sampled rows, against the oracle."""
     wl = dataclasses.replace(W.make(name), split_tokens=split)
     _, res = _run(wl, label=f"{name}-full-S{split}", one_call=True, stream_kv=not wl.shares_pages())
@@ -342,6 +344,42 @@ def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
             res = ds.results()
             compare_step(res, oracle_step(wl, split_tokens=split), budget=budget,
                          label=f"{wl.name} wg{max_wg} S{split}")
+
+
+@pytest.mark.parametrize("split,max_wg", [(512, 0), (1024, 0), (4096, 0), (512, 1), (1024, 3),
+                                           (2048, 2), (4096, 1)])
+def test_long_splits_run_as_pieces(split, max_wg):
+    """Splits of 32 to 256 pages run as consecutive 16-page pieces of one
+    task.  Contexts on both sides of piece and split boundaries; with few
+    workgroups a wavefront folds several multi-piece tasks (and group
+    changes) into its runs, whose staged page values cover more than one
+    piece.  Every output against the oracle, on the one-call step and on the
+    separate calls, with and without the budgeting outputs."""
+    from paged_kv_cache_07_amd import binding
+    from paged_kv_cache_07_amd.device import DecodeStep
+    ctx = [0, 1, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047, 4095, 4096, 4097, 9000]
+    cases = [W.custom(ctx, Hq=16, Hkv=4, d=128, seed=31, max_pages=600),
+             W.custom([3000, 17, 8200, 700], Hq=16, Hkv=2, d=64, dtype="bf16", seed=32),
+             W.make("b8_bimodal", ctx_divisor=16)]
+    opts = binding.make_opts(max_workgroups=max_wg) if max_wg else None
+    for wl in cases:
+        wl.s_prev = np.random.default_rng(6).standard_normal(wl.s_prev.shape).astype(np.float32)
+        ref = oracle_step(wl, split_tokens=split)
+        for budget, one_call, stream_kv in ((True, True, True), (True, False, False),
+                                            (False, True, False)):
+            say("pieces", wl.name, "split", split, "max_wg", max_wg, "budget", budget,
+                "one_call", one_call, "stream", stream_kv)
+            ds = DecodeStep(wl, budget=budget, split_tokens=split, stream_kv=stream_kv)
+            if one_call:
+                ds.step(opts=opts)
+            else:
+                ds.run()
+            res = ds.results()
+            tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, split)
+            assert res["n_tasks"] == n
+            assert np.array_equal(res["tasks"], tasks) and np.array_equal(res["group_offsets"], offs)
+            compare_step(res, ref, budget=budget,
+                         label=f"{wl.name} S{split} wg{max_wg} one_call={one_call}")
 
 
 @pytest.mark.parametrize("ctx,extra_pages,split,max_wg", [
