@@ -99,6 +99,7 @@ struct AttnParams {
   const float* s_prev;
   int32_t split_tokens, B, Hq, Hkv, G, max_pages, num_pages, capacity;
   int32_t nwaves;   // wavefronts in the grid
+  int32_t ncls;     // schedule classes (KV heads g % ncls), 1 or 8
   // Division by split_tokens and by the number of wavefronts in the grid.
   DivMagic div_split, div_waves;
   const kvpage_task* tasks;
@@ -485,26 +486,61 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   } else {
     ntask = min(p.n_tasks[0], p.capacity);
   }
-  // The queue is cut into chunks of c consecutive positions (c pieces of
+  // Classes: with ncls > 1 the queue is taken as ncls classes, class x the
+  // (sequence, KV head) groups with g % ncls == x in queue order, and class x
+  // runs on the workgroups with blockIdx.x % ncls == x.  Workgroups go to the
+  // 8 XCDs round robin, so all tasks of one KV head run on one XCD: a page
+  // that several sequences share (a common prefix) is fetched into that
+  // XCD's L2 once and served from there to the others.  It needs classes of
+  // equal size (fused queue, Hkv % ncls == 0, nothing cut by capacity) and
+  // a grid that is a multiple of ncls (checked on the host).
+  int ncls = 1;
+  if constexpr (FUSEDQ) ncls = (p.ncls > 1 && ntask == sq.total) ? p.ncls : 1;
+  const int cls = (int)blockIdx.x % ncls;
+  const int nwc = nwaves / ncls;                                        // wavefronts of the class
+  const int wc = ((int)blockIdx.x / ncls) * kWavesPerGroup + wave;   // this one's rank in it
+  const int T = ntask / ncls;                                           // positions of the class
+  // Class position j -> queue position: j falls in sequence b when b's
+  // class positions, [start_b, end_b) / ncls, hold it; inside b it is task
+  // s of the class's gi-th KV head, g = cls + ncls * gi.
+  auto pos_of = [&](int j) -> int {
+    if constexpr (FUSEDQ) {
+      if (ncls > 1) {
+        const uint64_t past = __builtin_amdgcn_ballot_w64(sq.incl > ncls * j);
+        const int bq = __builtin_ctzll(past);
+        const int start = __builtin_amdgcn_readlane(sq.incl - sq.cnt, bq);
+        const int ns = __builtin_amdgcn_readlane(sq.ns, bq);
+        const int rr = j - start / ncls;
+        const int gi = rr / ns;
+        return start + (cls + ncls * gi) * ns + (rr - gi * ns);
+      }
+    }
+    return j;
+  };
+  // The class is cut into chunks of c consecutive positions (c pieces of
   // work at most kRunMax, sized so every wavefront gets nearly the same
-  // number of chunks); wave gw runs chunks gw, gw + nwaves, ...  Run
-  // partials start at multiples of c.
+  // number of chunks); wavefront wc runs chunks wc, wc + nwc, ...  Run
+  // partials start at a group's first task and at the first task of every
+  // chunk.
   const int pieces = (p.split_tokens + PPT * kPage - 1) / (PPT * kPage);   // per task
   const int cmax = kRunMax / pieces;
   int c;
-  if (ntask <= nwaves * cmax) {   // one round
-    c = max(1, (int)div_by((uint32_t)(ntask + nwaves - 1), p.div_waves));
+  if (T <= nwc * cmax) {   // one round
+    c = max(1, ncls == 1 ? (int)div_by((uint32_t)(T + nwc - 1), p.div_waves) : (T + nwc - 1) / nwc);
   } else {
-    const int rounds = (ntask + nwaves * cmax - 1) / (nwaves * cmax);
-    c = (ntask + nwaves * rounds - 1) / (nwaves * rounds);
+    const int rounds = (T + nwc * cmax - 1) / (nwc * cmax);
+    c = (T + nwc * rounds - 1) / (nwc * rounds);
   }
-  if (blockIdx.x == 0 && wave == 0 && lane == 0) p.ws_hdr[0] = c;
-  int chunk = gw;
-  if (chunk * c >= ntask) return;   // chunk past the last one
-  int chunk_end = min((chunk + 1) * c, ntask);   // exclusive
-  const int t_first = chunk * c;
+  if (blockIdx.x == 0 && wave == 0 && lane == 0) {
+    p.ws_hdr[0] = c;
+    p.ws_hdr[1] = ncls;
+  }
+  int chunk = wc;
+  if (chunk * c >= T) return;   // chunk past the last one
+  int chunk_end = min((chunk + 1) * c, T);   // exclusive
+  int cj = chunk * c;                        // class position of the current task
 
-  Task cur = fetch(t_first);
+  Task cur = fetch(pos_of(cj));
   // Query rows first: they arrive with the page ids, so the operand is built
   // while the first tiles are in flight.
   const Rows rows = load_rows(cur);
@@ -514,7 +550,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   build_operand(rows, qop);
 
   // Run state: the running partial of consecutive tasks of one (b, g).
-  int run_start = t_first;
+  int run_start = cur.t;
   int run_lp0 = cur.lp0;
   int run_pages = 0;
   int run_units = 0;   // pieces of the run done so far
@@ -593,13 +629,12 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 
     // ---- the next piece of this wave (or this one again at the end) ----
     const bool more = !cur.last;   // another piece of this task
-    const bool in_chunk = more || cur.t + 1 < chunk_end;
-    const bool next_chunk = !in_chunk && (chunk + nwaves) * c < ntask;
+    const bool in_chunk = more || cj + 1 < chunk_end;
+    const bool next_chunk = !in_chunk && (chunk + nwc) * c < T;
     const bool has_next = in_chunk || next_chunk;
-    const int tn = more ? cur.t
-                        : (cur.t + 1 < chunk_end ? cur.t + 1
-                                                 : (next_chunk ? (chunk + nwaves) * c : cur.t));
-    const Task nxt = more ? unit(cur, cur.piece + 1) : fetch(tn);
+    const int jn = more ? cj
+                        : (cj + 1 < chunk_end ? cj + 1 : (next_chunk ? (chunk + nwc) * c : cj));
+    const Task nxt = more ? unit(cur, cur.piece + 1) : fetch(pos_of(jn));
     const int32_t ids_n = load_page_ids(nxt);
     const Rows rows_n = load_rows(nxt);
 
@@ -776,10 +811,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       }
       if (!has_next) break;
       if (next_chunk) {
-        chunk += nwaves;
-        chunk_end = min((chunk + 1) * c, ntask);
+        chunk += nwc;
+        chunk_end = min((chunk + 1) * c, T);
       }
-      run_start = tn;
+      run_start = nxt.t;
       run_lp0 = nxt.lp0;
       run_pages = 0;
       run_units = 0;
@@ -790,6 +825,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       build_operand(rows_n, qop);
     }
     cur = nxt;
+    cj = jn;
     ids = ids_n;
   }
 }
@@ -824,6 +860,11 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
   if (grid <= 0) return hipSuccess;
   AttnParams a = p;
   a.nwaves = grid * kWavesPerGroup;
+  // One class per XCD when the fused queue splits evenly over them and there
+  // is more than one sequence (only then can a page be shared).  Measured on
+  // MI355X: B64 with a shared prefix 3.4% faster, B8 workloads 1.3-2.1%; one
+  // 32K-token sequence 2.5% slower, hence not for B = 1.
+  a.ncls = (FUSEDQ && p.B >= 2 && p.Hkv % 8 == 0 && grid % 8 == 0) ? 8 : 1;
   a.div_waves = div_magic((uint32_t)grid * kWavesPerGroup);
   if (ev_start || ev_stop) {
     // Timestamps taken by the dispatch itself: start and end of this kernel.

@@ -128,17 +128,19 @@ __host__ __device__ inline size_t ws_bytes(int64_t cap, int G, int D) {
 }
 
 // Queue positions of the run partials of one (sequence, KV head) whose tasks
-// are [lo, hi), for run length c: lo, then every multiple of c inside.
-__host__ __device__ inline int run_count(int lo, int hi, int c) {
-  return hi <= lo ? 0 : 1 + (hi - 1) / c - lo / c;
+// are [lo, hi): lo, then lo + k for every k > 0 with (k + off) % c == 0,
+// where c is the run length (chunk size of the attention kernel's schedule)
+// and off the position of lo inside its chunk.
+__host__ __device__ inline int run_count(int lo, int hi, int c, int off) {
+  return hi <= lo ? 0 : 1 + (hi - lo - 1 + off) / c;
 }
-__host__ __device__ inline int run_slot(int lo, int i, int c) {
-  return i == 0 ? lo : (lo / c + i) * c;
+__host__ __device__ inline int run_slot(int lo, int i, int c, int off) {
+  return i == 0 ? lo : lo + i * c - off;
 }
 // The run start that holds queue position t of a group beginning at lo.
-__host__ __device__ inline int run_of(int lo, int t, int c) {
-  const int s = (t / c) * c;
-  return s > lo ? s : lo;
+__host__ __device__ inline int run_of(int lo, int t, int c, int off) {
+  const int s = ((t - lo + off) / c) * c - off;
+  return lo + (s > 0 ? s : 0);
 }
 
 }  // namespace kvpage

@@ -101,7 +101,7 @@ __device__ __forceinline__ int pages_of(int32_t ctx) {
 // the run partials of the group's task range [lo, lo + n).  All of a
 // workgroup's row metadata is requested at once.
 struct Row {
-  int b, h, g, hh, lo, n, runlen, nrun, npg;
+  int b, h, g, hh, lo, n, runlen, off, nrun, npg;
 };
 
 __device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pages) {
@@ -113,11 +113,25 @@ __device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pa
   const int lo = p.group_offsets[r.b * p.Hkv + r.g];
   const int hi = p.group_offsets[r.b * p.Hkv + r.g + 1];
   const int runlen = p.ws_hdr[0];
+  const int ncls = p.ws_hdr[1];
+  const int seq_lo = p.group_offsets[r.b * p.Hkv];
+  const int seq_lo1 = p.group_offsets[r.b * p.Hkv + 1];
   const int ctx = need_pages ? clamp_ctx(p.fin.ctx_lens[r.b], p.fin.max_pages) : 0;
   r.lo = min(max(lo, 0), p.capacity);
   r.n = max(min(hi, p.capacity) - r.lo, 0);
   r.runlen = max(1, runlen);
-  r.nrun = run_count(r.lo, r.lo + r.n, r.runlen);
+  // Where the group's first task sits inside its chunk of the schedule.  With
+  // the queue taken as ncls classes (KV heads g % ncls), class-local position
+  // of the group's first task: start / ncls + (g / ncls) * ns for the
+  // sequence's first queue position `start` and ns tasks per KV head.
+  if (ncls > 1 && p.Hkv % ncls == 0) {
+    const int start = max(seq_lo, 0);
+    const int ns = max(seq_lo1 - start, 0);
+    r.off = (start / ncls + (r.g / ncls) * ns) % r.runlen;
+  } else {
+    r.off = r.lo % r.runlen;
+  }
+  r.nrun = run_count(r.lo, r.lo + r.n, r.runlen, r.off);
   r.npg = pages_of(ctx);
   return r;
 }
@@ -126,7 +140,7 @@ __device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pa
 // arrays so that a load for a missing run (j >= nrun) stays in bounds.
 __device__ __forceinline__ int64_t run_index(const MergeParams& p, const Row& r, int j) {
   const int jj = min(j, max(r.nrun - 1, 0));
-  const int slot = min(run_slot(r.lo, jj, r.runlen), p.capacity - 1);
+  const int slot = min(run_slot(r.lo, jj, r.runlen, r.off), p.capacity - 1);
   return (int64_t)slot * p.G + r.hh;
 }
 
@@ -275,7 +289,7 @@ struct PageLoads {
     for (int k = 0; k < kPagesPerThread; ++k) {
       const int pg = min(slice * kPagesPerBlock + k * kMergeThreads + (int)threadIdx.x, last);
       raw[k] = mrow[pg];
-      const int run = run_of(r.lo, r.lo + pg / f.pages_per_split, r.runlen);
+      const int run = run_of(r.lo, r.lo + pg / f.pages_per_split, r.runlen, r.off);
       m[k] = p.ws_rm[(int64_t)min(run, p.capacity - 1) * p.G + r.hh];
     }
   }
@@ -439,7 +453,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergePa
     for (int k = 0; k < kWavePagesPerLane; ++k) {
       const int pg = min(slice * kPagesPerBlock + k * kWave + lane, last);
       raw[k] = mrow[pg];
-      const int run = run_of(r.lo, r.lo + pg / f.pages_per_split, r.runlen);
+      const int run = run_of(r.lo, r.lo + pg / f.pages_per_split, r.runlen, r.off);
       rmx[k] = p.ws_rm[(int64_t)min(run, p.capacity - 1) * p.G + r.hh];
     }
   }

@@ -104,6 +104,15 @@ class DecodeStep:
     def set_query(self, q_host: np.ndarray):
         self.q.copy_(host_to_device(q_host, self.wl.dtype, self.device))
 
+    def schedule_classes(self) -> int:
+        """Schedule classes the last attention launch used (workspace header
+        word 1): 8 when each KV head's tasks ran on one XCD, else 1.  Run
+        partials, and so the rounding of out, lse and page mass, follow the
+        schedule."""
+        torch = _torch()
+        torch.cuda.synchronize(self.device)
+        return int(self.workspace[4:8].view(torch.int32).item())
+
     # -- the three calls of a step --------------------------------------
     def build_queue(self, stream=None):
         K.kvpage_build_queue(self.shape, self.ctx_lens, self.tasks, self.capacity,

@@ -299,7 +299,12 @@ def test_repeat_runs_are_bitwise_identical_and_split_calls_match():
 @pytest.mark.parametrize("budget", [True, False])
 def test_one_call_step_equals_separate_calls(budget):
     """kvpage_decode_step (fused merge + finish, timed attention launch) gives
-    the same bits as kvpage_build_queue + kvpage_decode_attn + kvpage_page_mass."""
+    the same bits as kvpage_build_queue + kvpage_decode_attn + kvpage_page_mass
+    where both run the same schedule.  Where the one-call step runs one class
+    of KV heads per XCD (several sequences, Hkv a multiple of 8) its run
+    partials differ from the separate calls' linear schedule: the queue, page
+    maxima and summaries still agree bit for bit, out, lse and page mass to
+    rounding (and both match the oracle)."""
     from paged_kv_cache_07_amd import binding
     from paged_kv_cache_07_amd.device import DecodeStep
     for name, div in (("tiny", 1), ("b8_bimodal", 32), ("b64_prefix", 16), ("b8_zipf", 64)):
@@ -315,12 +320,19 @@ def test_one_call_step_equals_separate_calls(budget):
         rb = b.results()
         stop.synchronize()
         assert start.elapsed_ms(stop) > 0
-        keys = ["out_bits", "lse", "tasks", "group_offsets"] + (
-            ["mass", "page_max", "s_next"] if budget else [])
+        same = b.schedule_classes() == a.schedule_classes() == 1
+        assert b.schedule_classes() == (8 if wl.B >= 2 and wl.Hkv % 8 == 0 else 1), name
+        keys = ["tasks", "group_offsets"] + (["page_max", "s_next"] if budget else [])
+        keys += (["out_bits", "lse"] + (["mass"] if budget else [])) if same else []
         for key in keys:
             assert np.array_equal(ra[key], rb[key]), (name, key)
-        if budget:
-            compare_step(rb, oracle_step(wl), label=name)
+        if not same:
+            for key in ("out", "lse") + (("mass",) if budget else ()):
+                assert_close(key, rb[key], ra[key])
+        ref = oracle_step(wl)
+        compare_step(rb, ref, budget=budget, label=name)
+        if not same:
+            compare_step(ra, ref, budget=budget, label=name)
 
 
 @pytest.mark.parametrize("max_wg,split", [(1, 256), (3, 256), (1, 64), (3, 32), (2, 128)])
