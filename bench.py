@@ -72,16 +72,15 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
       * roofline: the split-attention kernel's own dispatch records its start
         and end (hipExtLaunchKernelGGL events) -> that kernel's duration.
     They are separate because kernel-level timestamps add a few microseconds
-    to a step.  stream_kv (KVPAGE_FLAG_STREAM_KV) defaults to "the tables
-    share no page".
+    to a step.  stream_kv (KVPAGE_FLAG_STREAM_KV) defaults to on; where the
+    tables share a prefix, its pages are named in kvpage_launch_opts
+    .shared_pages and load through the caches while the rest streams.
     """
     import torch
 
     from paged_kv_cache_07_amd import binding, workloads as W
     from paged_kv_cache_07_amd.device import DecodeStep
 
-    # Tables that share no page take the streaming tile loads
-    # (KVPAGE_FLAG_STREAM_KV); the prefix-sharing batch keeps cached loads.
     if isinstance(name, tuple) and name[0] == "custom":     # ("custom", contexts, split)
         _, ctx, split = name
         wl = W.custom(ctx, Hq=32, Hkv=8, d=128, seed=21)
@@ -96,8 +95,10 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
         wl = W.make(name)
         split_tokens = None
     if stream_kv is None:
-        stream_kv = not wl.shares_pages()
-    ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens, stream_kv=stream_kv)
+        stream_kv = True
+    shared = W.shared_leading_pages(wl) if (stream_kv and wl.shares_pages()) else None
+    ds = DecodeStep(wl, budget=budget, split_tokens=split_tokens, stream_kv=stream_kv,
+                    shared_pages=shared)
     kv = W.kv_bytes(wl)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -139,6 +140,7 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
         "page_size": wl.page_size, "split_tokens": wl.split_tokens, "dtype": wl.dtype,
         "ctx_total": int(wl.ctx_lens.sum()), "n_tasks": n_tasks, "kv_bytes": kv,
         "kv_bytes_unique": W.kv_bytes(wl, unique=True), "stream_kv": stream_kv,
+        "shared_prefix_cached": shared is not None,
         "step_ms_mean": float(step_ms.mean()), "step_ms_p50": float(np.median(step_ms)),
         "step_ms_p10": float(np.percentile(step_ms, 10)), "step_ms_p90": float(np.percentile(step_ms, 90)),
         "attn_ms_mean": float(attn_ms.mean()), "attn_ms_p50": float(np.median(attn_ms)),
@@ -414,7 +416,8 @@ def main():
             "step_ms_mean": r["step_ms_mean"], "attn_ms_mean": r["attn_ms_mean"],
             "kv_bytes": r["kv_bytes"], "kv_bytes_unique": r["kv_bytes_unique"],
             "n_tasks": r["n_tasks"], "B": r["B"], "Hq": r["Hq"], "Hkv": r["Hkv"],
-            "dtype": r["dtype"], "stream_kv": r["stream_kv"], "steps": k,
+            "dtype": r["dtype"], "stream_kv": r["stream_kv"],
+            "shared_prefix_cached": r["shared_prefix_cached"], "steps": k,
         }
 
     # The split policy (kvpage_choose_split) beside the fixed 256-token split,

@@ -46,7 +46,7 @@ class kvpage_budget(ctypes.Structure):
 
 class kvpage_launch_opts(ctypes.Structure):
     _fields_ = [("attn_start", ctypes.c_void_p), ("attn_stop", ctypes.c_void_p),
-                ("max_workgroups", ctypes.c_int32)]
+                ("max_workgroups", ctypes.c_int32), ("shared_pages", ctypes.c_void_p)]
 
 
 class KvpageError(RuntimeError):
@@ -304,6 +304,9 @@ class HipEvent:
 
 
 def make_opts(start: HipEvent | None = None, stop: HipEvent | None = None,
-              max_workgroups: int = 0) -> kvpage_launch_opts:
+              max_workgroups: int = 0, shared_pages=None) -> kvpage_launch_opts:
+    """shared_pages: None or a device int32 [B] tensor (or address)."""
     return kvpage_launch_opts(start.handle if start else None, stop.handle if stop else None,
-                              max_workgroups)
+                              max_workgroups,
+                              shared_pages if isinstance(shared_pages, (int, type(None)))
+                              else shared_pages.data_ptr())

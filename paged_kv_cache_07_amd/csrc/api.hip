@@ -23,7 +23,8 @@ hipError_t launch_gather_offsets(const kvpage_shape&, const int32_t*, const kvpa
 hipError_t launch_split_attn(const kvpage_shape&, const void*, const void*, const void*,
                              const int32_t*, const kvpage_task*, const int32_t*, int32_t, void*,
                              const kvpage_budget*, hipStream_t, hipEvent_t, hipEvent_t,
-                             const int32_t*, kvpage_task*, int32_t*, int32_t*, int32_t);
+                             const int32_t*, kvpage_task*, int32_t*, int32_t*, int32_t,
+                             const int32_t*);
 bool split_attn_can_fuse_queue(const kvpage_shape&);
 hipError_t launch_append(const kvpage_shape&, const void*, const void*, void*, void*, int32_t*,
                          const int32_t*, int32_t*, const int32_t*, const int32_t*, int32_t*,
@@ -201,7 +202,7 @@ int kvpage_split_attn(const kvpage_shape* s, const void* q, const void* k_pool, 
   if (s->B == 0 || capacity == 0) return KVPAGE_OK;
   return status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks, capacity,
                                      workspace, budget, stream, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, 0));
+                                     nullptr, nullptr, 0, nullptr));
 }
 
 int kvpage_merge_splits(const kvpage_shape* s, const int32_t* group_offsets, int32_t capacity,
@@ -228,7 +229,7 @@ int kvpage_decode_attn(const kvpage_shape* s, const void* q, const void* k_pool,
   if (capacity > 0) {
     KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
                                        capacity, workspace, budget, stream, nullptr, nullptr,
-                                       nullptr, nullptr, nullptr, nullptr, 0)));
+                                       nullptr, nullptr, nullptr, nullptr, 0, nullptr)));
   }
   return status_of(launch_merge(*s, group_offsets, capacity, workspace, out, lse, stream));
 }
@@ -247,18 +248,22 @@ int kvpage_decode_step(const kvpage_shape* s, const void* q, const void* k_pool,
   hipEvent_t t1 = opts ? opts->attn_stop : nullptr;
   const int max_wg = opts ? opts->max_workgroups : 0;
   if (max_wg < 0) return KVPAGE_ERR_INVALID_ARG;
+  // Shared leading pages matter only with streaming loads (else every load
+  // goes through the caches already).
+  const int32_t* shared =
+      (opts && (s->flags & KVPAGE_FLAG_STREAM_KV)) ? opts->shared_pages : nullptr;
   if (capacity > 0 && split_attn_can_fuse_queue(*s)) {
     // The attention kernel builds the queue itself (same content, same order).
     KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
                                        capacity, workspace, budget, stream, t0, t1, ctx_lens,
-                                       tasks, group_offsets, n_tasks, max_wg)));
+                                       tasks, group_offsets, n_tasks, max_wg, shared)));
   } else {
     KV_TRY(status_of(launch_build_queue(*s, ctx_lens, tasks, capacity, group_offsets, n_tasks,
                                         stream)));
     if (capacity > 0) {
       KV_TRY(status_of(launch_split_attn(*s, q, k_pool, v_pool, block_tables, tasks, n_tasks,
                                          capacity, workspace, budget, stream, t0, t1, nullptr,
-                                         nullptr, nullptr, nullptr, max_wg)));
+                                         nullptr, nullptr, nullptr, max_wg, shared)));
     }
   }
   if (budget)

@@ -31,6 +31,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include <hip/hip_ext.h>
 
@@ -100,6 +101,9 @@ struct AttnParams {
   int32_t split_tokens, B, Hq, Hkv, G, max_pages, num_pages, capacity;
   int32_t nwaves;   // wavefronts in the grid
   int32_t ncls;     // schedule classes (KV heads g % ncls), 1 or 8
+  // Per sequence, leading logical pages that other sequences may share
+  // (loads kLoadsPrefix only).
+  const int32_t* shared_pages;
   // Division by split_tokens and by the number of wavefronts in the grid.
   DivMagic div_split, div_waves;
   const kvpage_task* tasks;
@@ -165,6 +169,13 @@ __device__ __forceinline__ uint32_t pick_pair(uint32_t a, uint32_t b, bool hi_ha
 // One tile load.  With STREAM the access is marked non-temporal, so the lines
 // stream past the caches instead of displacing what is reused (page ids,
 // query rows, partials).  Only right when no page is read twice in a call.
+// Tile load policies of a kernel instance: all through the caches, all
+// streaming, or streaming except the shared leading pages of each sequence
+// (chosen per piece of work).
+constexpr int kLoadsCached = 0;
+constexpr int kLoadsStream = 1;
+constexpr int kLoadsPrefix = 2;
+
 template <bool STREAM, typename V>
 __device__ __forceinline__ V tile_load(const char* addr) {
   if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const V*>(addr));
@@ -207,7 +218,7 @@ __device__ __forceinline__ SeqScan scan_lengths(int32_t raw, int B, int Hkv, int
   return q;
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, int LOADS>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const AttnParams p) {
   using E = Elem<BF>;
@@ -272,7 +283,9 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   // tb0 / te are the task's token range, tok_begin / tok_end the piece's.
   struct Task {
     int t, b, g, tok_begin, tok_end, ntok, npg, lp0, piece, tb0, te;
-    bool last;   // the task's last piece
+    int sp;        // shared leading pages of sequence b (kLoadsPrefix)
+    bool last;     // the task's last piece
+    bool cached;   // loads through the caches (kLoadsPrefix: the piece starts on a shared page)
   };
   auto unit = [&](Task k, int pc) {
     k.piece = pc;
@@ -282,6 +295,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     k.npg = (k.ntok + kPage - 1) / kPage;
     k.lp0 = k.tok_begin / kPage;
     k.last = k.tok_end >= k.te;
+    k.cached = LOADS == kLoadsPrefix && k.lp0 < k.sp;
     return k;
   };
   SeqScan sq = {0, 0, 0, 0, 0};
@@ -322,6 +336,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     k.g = tk.kv_head;
     k.tb0 = tk.tok_begin;
     k.te = tk.tok_end;
+    k.sp = 0;
+    if constexpr (LOADS == kLoadsPrefix) k.sp = p.shared_pages[k.b];
     return unit(k, 0);
   };
   // Lane i < npg holds the physical id of the task's page i.
@@ -357,7 +373,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   };
   // Tile tau of a task: K page tau for tau < 16, V page tau - 16 after.  Pages
   // past npg - 1 repeat the last page (the load count never depends on npg).
-  auto load_tile = [&](const Task& k, int32_t ids, int tau, uint32_t (&dst)[TW]) {
+  // sl: std::true_type for non-temporal (streaming) loads, false_type for
+  // loads through the caches.
+  auto load_tile = [&](auto sl, const Task& k, int32_t ids, int tau, uint32_t (&dst)[TW]) {
+    constexpr bool SL = decltype(sl)::value;
     const bool is_v = tau >= PPT;
     const int pg = max(min(is_v ? tau - PPT : tau, k.npg - 1), 0);
     const int32_t pid = clamp_page(__builtin_amdgcn_readlane(ids, pg), p.num_pages);
@@ -366,7 +385,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       const char* base = kpool + off;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const u32x4 w = tile_load<STREAM, u32x4>(base + koff[kb]);
+        const u32x4 w = tile_load<SL, u32x4>(base + koff[kb]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) dst[4 * kb + x] = w[x];
       }
@@ -375,11 +394,11 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (VW == 4) {
-          const u32x4 w = tile_load<STREAM, u32x4>(base + voff[e]);
+          const u32x4 w = tile_load<SL, u32x4>(base + voff[e]);
 #pragma unroll
           for (int x = 0; x < 4; ++x) dst[VW * e + x] = w[x];
         } else {
-          const u32x2 w = tile_load<STREAM, u32x2>(base + voff[e]);
+          const u32x2 w = tile_load<SL, u32x2>(base + voff[e]);
 #pragma unroll
           for (int x = 0; x < VW; ++x) dst[VW * e + x] = w[x];
         }
@@ -540,13 +559,26 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   int chunk_end = min((chunk + 1) * c, T);   // exclusive
   int cj = chunk * c;                        // class position of the current task
 
+  // Runs f with the load policy of task k: one uniform branch per task, so
+  // that no tile load sits under a branch of its own.
+  auto with_policy = [&](const Task& k, auto f) __attribute__((always_inline)) {
+    if constexpr (LOADS == kLoadsPrefix) {
+      if (k.cached) return f(std::false_type{});
+      return f(std::true_type{});
+    } else {
+      return f(std::integral_constant<bool, LOADS == kLoadsStream>{});
+    }
+  };
+
   Task cur = fetch(pos_of(cj));
   // Query rows first: they arrive with the page ids, so the operand is built
   // while the first tiles are in flight.
   const Rows rows = load_rows(cur);
   int32_t ids = load_page_ids(cur);
+  with_policy(cur, [&](auto sl) __attribute__((always_inline)) {
 #pragma unroll
-  for (int tau = 0; tau < DEPTH; ++tau) load_tile(cur, ids, tau, buf[tau]);
+    for (int tau = 0; tau < DEPTH; ++tau) load_tile(sl, cur, ids, tau, buf[tau]);
+  });
   build_operand(rows, qop);
 
   // Run state: the running partial of consecutive tasks of one (b, g).
@@ -564,7 +596,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
 #pragma unroll
   for (int j = 0; j < VD; ++j) O[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  while (true) {
+  // One piece of work: pass 1, pass 2, staging and (at a run boundary) the
+  // partial.  Returns false after the wavefront's last piece.
+  auto step = [&](auto sl) __attribute__((always_inline)) -> bool {
+    constexpr bool SL = decltype(sl)::value;
     const int b = cur.b, g = cur.g, ntok = cur.ntok, npg = cur.npg;
 
     // ---- pass 1: scores of every page; page max (budget) and task max ----
@@ -580,7 +615,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int x = 0; x < 4; ++x) a[kb][x] = buf[slot][4 * kb + x];
-      if (i + DEPTH < NT) load_tile(cur, ids, i + DEPTH, buf[slot]);
+      if (i + DEPTH < NT) load_tile(sl, cur, ids, i + DEPTH, buf[slot]);
       if (i < npg) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -672,7 +707,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         vop[j][1] = used ? pick_pair(buf[slot][2 * VW + w], buf[slot][3 * VW + w], hi) : 0u;
       }
       if (tau + DEPTH < NT) {
-        load_tile(cur, ids, tau + DEPTH, buf[slot]);
+        load_tile(sl, cur, ids, tau + DEPTH, buf[slot]);
       } else {
         // The next task's first K tiles; with no next task, the same number of
         // loads re-read this task's last V tile (just fetched, so cached).
@@ -681,7 +716,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         const char* base = (has_next ? kpool : vpool) + tile_offset(pid, has_next ? nxt.g : g, p.Hkv, D) * 2;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 w = tile_load<STREAM, u32x4>(base + koff[kb]);
+          const u32x4 w = tile_load<SL, u32x4>(base + koff[kb]);
 #pragma unroll
           for (int x = 0; x < 4; ++x) buf[slot][4 * kb + x] = w[x];
         }
@@ -809,7 +844,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           }
         }
       }
-      if (!has_next) break;
+      if (!has_next) return false;
       if (next_chunk) {
         chunk += nwc;
         chunk_end = min((chunk + 1) * c, T);
@@ -827,13 +862,16 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     cur = nxt;
     cj = jn;
     ids = ids_n;
+    return true;
+  };
+  while (with_policy(cur, step)) {
   }
 }
 
-template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, bool STREAM>
+template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, int LOADS>
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
-  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, STREAM>;
+  auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, LOADS>;
   // Resident workgroups of this instance per device, found once.  Concurrent
   // first calls may both look it up; they store the same value.
   static std::atomic<int> resident_wg[64];
@@ -884,36 +922,36 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
 #define KVPAGE_ATTN_DEPTH 2
 #endif
 
-template <bool FUSEDQ, int PPT, bool STREAM>
+template <bool FUSEDQ, int PPT, int LOADS>
 static hipError_t dispatch_ppt(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                                hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                                int max_wg) {
   constexpr int DP = KVPAGE_ATTN_DEPTH < PPT ? KVPAGE_ATTN_DEPTH : PPT;
   const bool bf = s.dtype == KVPAGE_BF16;
   if (s.d == 128) {
-    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                       : launch_one<128, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
-    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-               : launch_one<128, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    if (bf) return bud ? launch_one<128, true, true, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                       : launch_one<128, true, false, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg);
+    return bud ? launch_one<128, false, true, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg)
+               : launch_one<128, false, false, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg);
   }
-  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-                     : launch_one<64, true, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
-  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg)
-             : launch_one<64, false, false, DP, FUSEDQ, PPT, STREAM>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  if (bf) return bud ? launch_one<64, true, true, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg)
+                     : launch_one<64, true, false, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg);
+  return bud ? launch_one<64, false, true, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg)
+             : launch_one<64, false, false, DP, FUSEDQ, PPT, LOADS>(p, capacity, stream, ev_start, ev_stop, max_wg);
 }
 
 // The instance with the fewest pages per task that holds one split: a task
 // issues loads for all of its instance's pages, so a short split run by the
 // 16-page instance would spend most of its loads on repeats.  Splits longer
 // than 16 pages run on the 16-page instance as consecutive pieces.
-template <bool FUSEDQ, bool STREAM>
+template <bool FUSEDQ, int LOADS>
 static hipError_t dispatch(const kvpage_shape& s, const AttnParams& p, int capacity, bool bud,
                            hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                            int max_wg) {
   const int pages = s.split_tokens / kPage;
-  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return dispatch_ppt<FUSEDQ, 16, STREAM>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 4) return dispatch_ppt<FUSEDQ, 4, LOADS>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  if (pages <= 8) return dispatch_ppt<FUSEDQ, 8, LOADS>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  return dispatch_ppt<FUSEDQ, 16, LOADS>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
 }
 
 // Wavefronts of one resident round per compute unit (one workgroup per CU).
@@ -933,7 +971,8 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
                              void* workspace, const kvpage_budget* budget, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, const int32_t* ctx_lens,
                              kvpage_task* tasks_out, int32_t* group_offsets_out,
-                             int32_t* n_tasks_out, int32_t max_wg) {
+                             int32_t* n_tasks_out, int32_t max_wg,
+                             const int32_t* shared_pages) {
   const int G = s.Hq / s.Hkv;
   const WorkspaceView ws = ws_view(workspace, capacity, G, s.d);
   AttnParams p;
@@ -973,11 +1012,16 @@ hipError_t launch_split_attn(const kvpage_shape& s, const void* q, const void* k
   const bool fused = tasks_out != nullptr;
   const bool bud = budget != nullptr;
   const bool stream_kv = (s.flags & KVPAGE_FLAG_STREAM_KV) != 0;
-  if (fused)
-    return stream_kv ? dispatch<true, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-              : dispatch<true, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
-  return stream_kv ? dispatch<false, true>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
-            : dispatch<false, false>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg);
+  p.shared_pages = shared_pages;
+  const int loads = !stream_kv ? kLoadsCached : (shared_pages ? kLoadsPrefix : kLoadsStream);
+#define KV_DISPATCH(F, L) dispatch<F, L>(s, p, capacity, bud, stream, ev_start, ev_stop, max_wg)
+  if (fused) {
+    if (loads == kLoadsPrefix) return KV_DISPATCH(true, kLoadsPrefix);
+    return loads == kLoadsStream ? KV_DISPATCH(true, kLoadsStream) : KV_DISPATCH(true, kLoadsCached);
+  }
+  if (loads == kLoadsPrefix) return KV_DISPATCH(false, kLoadsPrefix);
+  return loads == kLoadsStream ? KV_DISPATCH(false, kLoadsStream) : KV_DISPATCH(false, kLoadsCached);
+#undef KV_DISPATCH
 }
 
 }  // namespace kvpage

@@ -40,7 +40,8 @@ class DecodeStep:
     flips them for the next step.
     """
 
-    def __init__(self, wl, device="cuda", budget=True, split_tokens=None, stream_kv=False):
+    def __init__(self, wl, device="cuda", budget=True, split_tokens=None, stream_kv=False,
+                 shared_pages=None):
         torch = _torch()
         self.wl = wl
         self.device = torch.device(device)
@@ -65,6 +66,11 @@ class DecodeStep:
         out_dtype = torch.float16 if wl.dtype == "f16" else torch.bfloat16
         self.out = torch.zeros((wl.B, wl.Hq, wl.d), dtype=out_dtype, device=dev)
         self.lse = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device=dev)
+        # shared_pages: None, or per sequence the leading table pages other
+        # sequences may share (kvpage_launch_opts.shared_pages; with stream_kv
+        # those pages load through the caches, the rest stream).
+        self.shared_pages = None if shared_pages is None else torch.from_numpy(
+            np.ascontiguousarray(shared_pages, dtype=np.int32)).to(dev)
         self.use_budget = budget
         if budget:
             self.page_mass = torch.zeros((wl.B, wl.Hq, wl.max_pages), dtype=torch.float32, device=dev)
@@ -142,12 +148,21 @@ class DecodeStep:
         if self.use_budget:
             self.page_mass_finish(stream)
 
+    def launch_opts(self, opts=None):
+        """opts with this step's shared_pages filled in (a new one if None)."""
+        if self.shared_pages is None:
+            return opts
+        if opts is None:
+            opts = K.make_opts()
+        opts.shared_pages = self.shared_pages.data_ptr()
+        return opts
+
     def step(self, opts=None, stream=None):
         """The whole step in one call (queue, split attention, fused merge+finish)."""
         K.kvpage_decode_step(self.shape, self.q, self.k_pool, self.v_pool, self.block_tables,
                              self.ctx_lens, self.tasks, self.group_offsets, self.n_tasks,
                              self.capacity, self.workspace, self.budget, self.out, self.lse,
-                             opts, stream)
+                             self.launch_opts(opts), stream)
 
     # -- KV append (the step before attention) ----------------------------
     def set_free_list(self, free_pages: np.ndarray):

@@ -121,6 +121,12 @@ class Workload:
         return len(self.referenced_pages()) < n
 
 
+def shared_leading_pages(wl: Workload) -> np.ndarray:
+    """Per sequence, the leading table pages that other sequences share."""
+    pages = (wl.ctx_lens.astype(np.int64) + wl.page_size - 1) // wl.page_size
+    return np.minimum(pages, wl.shared_prefix_pages).astype(np.int32)
+
+
 def kv_bytes(wl: Workload, unique: bool = False) -> int:
     """Algorithmic K+V bytes one decode step must read.
 

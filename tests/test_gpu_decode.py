@@ -158,12 +158,19 @@ def test_oracle_sized_configs_all_outputs(name, div):
                                         ("b4_bimodal", 1024), ("b8_uniform", 1024)])
 def test_full_size_sampled_rows(name, split):
     """Full-size workloads in the launch configurations bench.py times (one
-    kvpage_decode_step call, streaming tile loads unless pages are shared;
+    kvpage_decode_step call, streaming tile loads except a shared prefix's;
     the B8 and B4 workloads also at the splits the policy picks for them,
     run as 16-page pieces): one query head of
     every (sequence, KV head) group, plus sampled rows, against the oracle."""
     wl = dataclasses.replace(W.make(name), split_tokens=split)
-    _, res = _run(wl, label=f"{name}-full-S{split}", one_call=True, stream_kv=not wl.shares_pages())
+    if wl.shares_pages():   # streaming except the shared prefix pages, as the benchmark runs it
+        from paged_kv_cache_07_amd.device import DecodeStep
+        say("run", name, "full", "split", split, "shared prefix loads")
+        ds = DecodeStep(wl, stream_kv=True, shared_pages=W.shared_leading_pages(wl))
+        ds.step()
+        res = ds.results()
+    else:
+        _, res = _run(wl, label=f"{name}-full-S{split}", one_call=True, stream_kv=True)
     tasks, offs, n = kvref.build_queue(wl.ctx_lens, wl.Hkv, wl.split_tokens)
     assert res["n_tasks"] == n
     assert np.array_equal(res["tasks"], tasks) and np.array_equal(res["group_offsets"], offs)
@@ -554,6 +561,37 @@ def test_stream_kv_changes_no_bits(case, one_call):
     for key in ("tasks", "group_offsets", "out_bits", "lse", "mass", "page_max", "s_next"):
         assert np.array_equal(a[key], b[key]), key
     compare_step(b, oracle_step(wl), label=case)
+
+
+@pytest.mark.parametrize("case,split", [("b64_prefix_small", 256), ("b64_prefix_small", 1024),
+                                        ("edge", 256), ("edge", 512), ("edge", 64)])
+def test_shared_prefix_loads_change_no_bits(case, split):
+    """KVPAGE_FLAG_STREAM_KV with kvpage_launch_opts.shared_pages: pieces of
+    work that start on one of a sequence's shared leading pages load through
+    the caches, the rest stream.  Every output is bit-identical to all loads
+    cached (same schedule), and matches the oracle.  The edge case gives
+    every sequence its own count: none, one page, mid-split, mid-piece, past
+    the end of the context, and the whole table row."""
+    from paged_kv_cache_07_amd.device import DecodeStep
+    if case == "edge":
+        ctx = [0, 1, 300, 17, 4100, 2048, 9000, 513, 6000, 700, 4096, 15000]
+        wl = W.custom(ctx, Hq=16, Hkv=8, d=128, dtype="bf16", seed=33, max_pages=1000)
+        shared = np.array([0, 1, 0, 2, 40, 128, 100, 3, 5, 1000, 256, 937], dtype=np.int32)
+    else:
+        wl = W.make("b64_prefix", ctx_divisor=16)
+        shared = W.shared_leading_pages(wl)
+    wl.s_prev = np.random.default_rng(15).standard_normal(wl.s_prev.shape).astype(np.float32)
+    say("shared-prefix loads", case, "split", split)
+    a = DecodeStep(wl, split_tokens=split)
+    a.step()
+    ra = a.results()
+    b = DecodeStep(wl, split_tokens=split, stream_kv=True, shared_pages=shared)
+    b.step()
+    rb = b.results()
+    assert a.schedule_classes() == b.schedule_classes()
+    for key in ("tasks", "group_offsets", "out_bits", "lse", "mass", "page_max", "s_next"):
+        assert np.array_equal(ra[key], rb[key]), key
+    compare_step(rb, oracle_step(wl, split_tokens=split), label=f"{case} S{split}")
 
 
 @pytest.mark.parametrize("Hq,Hkv,d,dtype,ctx,extra_pages,split", [
