@@ -261,7 +261,6 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   const int r = lane >> 4;       // row of 16 lanes
   const int n = lane & 15;       // column inside the row
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * kWavesPerGroup + wave;
   const int nwaves = p.nwaves;   // gridDim would add the 256-byte hidden argument block
   const int G = p.G;
   const bool is_head = n < G;
@@ -785,6 +784,10 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     // ---- run boundary: write the run's partial (m, l, o) per head ----
     const bool new_group = nxt.b != b || nxt.g != g;
     if (!in_chunk || new_group) {
+      // The run's stores wait for issue slots behind the tile loads of the
+      // compute unit's other wavefronts; raised priority lets them go first
+      // (B1 0.3-0.6% faster, B8 unchanged, interleaved).
+      __builtin_amdgcn_s_setprio(3);
       const float ltot = rows_sum(l);
       if (r == 0 && is_head) {
         p.ws_rm[(int64_t)run_start * G + n] = mrun;
@@ -844,6 +847,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (!has_next) return false;
       if (next_chunk) {
         chunk += nwc;
