@@ -319,24 +319,28 @@ int kvpage_debug_gather_offsets(const kvpage_shape* shape, const int32_t* block_
  * side by side close together in time, from cache: on a batch sharing a
  * prefix, 256 ran 1.7% faster than 1024).  Only splits whose queue holds at
  * least one task per resident wavefront of the attention kernel
- * (n = Hkv * sum_b ceil(ctx_b / S) >= wavefronts) qualify.  Under the
- * kernel's schedule the busiest wavefront takes c * rounds positions, with
- * rounds = ceil(n / (m * wavefronts)), c = ceil(n / (rounds * wavefronts))
- * and m = 16 / ceil(S / 256) positions per chunk at most, each of at most
- * S / 16 pages.  Cost in pages: max(P / wavefronts, busiest pages / 1.5) +
- * f * c * rounds, where P = Hkv * sum_b ceil(ctx_b / 16) is the step's
- * pages (the kernel is bound by HBM, and a wavefront streams 1.5-1.8x
- * faster once the others have finished) and f the fixed cost of a position
- * (measured: half a page with streaming loads, one and a half cached).
- * Returns the cheapest, ties to the longer split; the page size (16) if no
- * split fills the wavefronts, 256 if every context is empty.  Measured on
- * MI355X against 256: 4 long + 4 short sequences 1024 (2.3% faster
- * attention), Zipf lengths 2048 (4.1%), 4 bimodal sequences 1024 (2.8%);
- * one 32768-token sequence keeps 256 (512 leaves half the wavefronts idle:
- * 26% slower).
+ * (Hkv * sum_b ceil(ctx_b / S) >= wavefronts) qualify.  Each is priced by
+ * simulating the kernel's schedule (per-XCD classes of KV heads where the
+ * kernel uses them; chunks of positions, at most 16 / ceil(S / 256) per
+ * chunk): every wavefront's pages plus a fixed cost per queue position
+ * (measured: half a page with streaming loads, one and a half cached), then
+ * the time to finish when each unfinished wavefront streams at
+ * min(1.43, wavefronts / unfinished) times its equal share of HBM (water
+ * filling: the kernel is bound by HBM, and a wavefront streams up to ~1.4-1.8x
+ * faster once others have finished).  Returns the cheapest, ties to the
+ * longer split; the page size (16) if no split fills the wavefronts, 256 if
+ * every context is empty.  Measured on MI355X against 256: 4 long + 4 short
+ * sequences 1024 (2.3% faster attention), Zipf lengths 2048 (4.1%), 4
+ * bimodal sequences 1024 (2.8%); one 32768-token sequence keeps 256 (512
+ * leaves half the wavefronts idle: 26% slower), and so do 64 sequences of
+ * 2-14K private tokens (1024: 6.8% slower, many wavefronts with six 64-page
+ * tasks).  Host cost: ~0.1 ms per call.
  *   shape: B, Hq, Hkv, d, page_size, max_pages, num_pages, dtype, scale and
- *     flags as for the other calls (flags as the step will use them);
- *     split_tokens is ignored.
+ *     flags as for the other calls: KVPAGE_FLAG_STREAM_KV set only when no
+ *     page is shared at all.  A step that names shared leading pages
+ *     (kvpage_launch_opts.shared_pages) still shares them: ask with the flag
+ *     clear (B64 with a shared prefix and shared_pages: 256 tokens 4.4%
+ *     faster than 1024).  split_tokens is ignored.
  *   ctx_lens_host: HOST array of B context lengths, each in [0, max_pages *
  *     page_size].
  *   wavefronts: resident wavefronts to fill; <= 0 queries the current device

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include "kvpage_common.h"
 
@@ -346,6 +347,81 @@ int kvpage_budget_decide(const kvpage_shape* s, const float* page_max, const int
                                         decision, victim, stream));
 }
 
+// ---- Split policy --------------------------------------------------------
+//
+// The attention kernel is bound by HBM: with every wavefront streaming, each
+// gets an equal share of the bandwidth, and once some have finished the rest
+// stream faster, up to kWaveRateCap times that share (measured on MI355X: a
+// wavefront reads 0.77 pages/us when 1024 stream and 1.37 pages/us when 256
+// do; the value below fits the split timings of the B1, B4, B8 and B64
+// workloads best).  A split is priced by simulating the kernel's schedule:
+// each wavefront's pages plus a fixed cost per queue position, then the
+// time to finish when every unfinished wavefront streams at
+// min(cap, wavefronts / unfinished) (water filling), in units of one page at
+// the equal share.
+constexpr double kWaveRateCap = 1.43;
+constexpr int64_t kSimRoundsMax = 8;   // past this, the wavefronts' loads are taken as equal
+
+static double water_fill(std::vector<double>& load) {
+  std::sort(load.begin(), load.end());
+  const double n = (double)load.size();
+  double t = 0.0, done = 0.0;
+  for (size_t i = 0; i < load.size(); ++i) {
+    const double active = n - (double)i;
+    const double rate = std::min(kWaveRateCap, n / active);
+    t += (load[i] - done) / rate;
+    done = load[i];
+  }
+  return t;
+}
+
+// Cost of split S (tokens, a multiple of the page size), or a negative value
+// if its queue has fewer tasks than wavefronts.  The schedule mirrors the
+// attention kernel's: with more than one sequence, at most 64 (fused queue
+// build), Hkv a multiple of 8 and wavefronts a multiple of 32, 8 classes of
+// KV heads each on its own wavefronts (identical, so one is simulated);
+// chunks of c positions per class, at most 16 pieces of 16 pages each.
+static double split_cost(const kvpage_shape& t, const int32_t* ctx, int32_t S, int64_t waves,
+                         double fixed) {
+  const int P = t.page_size;
+  const int ncls = (t.B >= 2 && t.B <= 64 && t.Hkv % 8 == 0 && waves % 32 == 0) ? 8 : 1;
+  const int64_t hpc = t.Hkv / ncls, nwc = waves / ncls;
+  // Per sequence: class positions and pages before it (prefix sums).
+  std::vector<int64_t> pos(t.B + 1, 0), pages(t.B + 1, 0);
+  for (int b = 0; b < t.B; ++b) {
+    pos[b + 1] = pos[b] + hpc * ((ctx[b] + S - 1) / S);
+    pages[b + 1] = pages[b] + hpc * ((ctx[b] + P - 1) / P);
+  }
+  const int64_t T = pos[t.B];
+  if (T * ncls < waves) return -1.0;
+  const int64_t cmax = split_attn_chunk_max(S);
+  int64_t rounds = 1, c;
+  if (T <= nwc * cmax) {
+    c = (T + nwc - 1) / nwc;
+  } else {
+    rounds = (T + nwc * cmax - 1) / (nwc * cmax);
+    c = (T + nwc * rounds - 1) / (nwc * rounds);
+  }
+  if (rounds > kSimRoundsMax)   // many chunks per wavefront: equal loads
+    return ((double)pages[t.B] + fixed * (double)T) / (double)nwc;
+  // Pages of class positions [0, p): sequence b holds positions
+  // [pos[b], pos[b+1]), hpc KV heads of n tasks each, all full splits but
+  // the last.
+  auto prefix = [&](int64_t p) -> int64_t {
+    const int b = (int)(std::upper_bound(pos.begin(), pos.end(), p) - pos.begin()) - 1;
+    if (b >= t.B) return pages[t.B];
+    const int64_t n = (ctx[b] + S - 1) / S;
+    const int64_t r = p - pos[b], gi = r / n, j = r - gi * n;
+    return pages[b] + gi * ((ctx[b] + P - 1) / P) + j * (S / P);
+  };
+  std::vector<double> load(nwc, 0.0);
+  for (int64_t k = 0; k * c < T; ++k) {
+    const int64_t a = k * c, e = std::min(a + c, T);
+    load[k % nwc] += (double)(prefix(e) - prefix(a)) + fixed * (double)(e - a);
+  }
+  return water_fill(load);
+}
+
 int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
                             int32_t wavefronts) {
   if (!s) return KVPAGE_ERR_INVALID_ARG;
@@ -370,42 +446,24 @@ int32_t kvpage_choose_split(const kvpage_shape* s, const int32_t* ctx_lens_host,
     waves = (int64_t)cus * split_attn_waves_per_cu();
   }
   if (total == 0) return 16 * t.page_size;
-  // Every candidate split from the longest the kernel runs down to the page
-  // size is priced by the busiest wavefront under the attention kernel's
-  // schedule (rounds of chunks of at most chunk_max positions): n queue
-  // positions of at most `split` tokens each.  The kernel is bound by HBM, so
-  // the cost is the larger of the mean pages per wavefront (the same for
-  // every split) and the busiest wavefront's pages over 1.5: a wavefront
-  // streams 1.5-1.8x faster once the others have finished (measured on
-  // MI355X: 16 pages per wavefront over 1024 of them, 0.77 pages/us each; 64
-  // over 256, 1.37).  Each position adds a fixed cost, measured at half a page
-  // with streaming loads and one and a half with cached ones.  Only splits
-  // with a task for every resident wavefront qualify; ties go to the longer
-  // split; none qualifies: the page size.  Where pages may be shared (cached
-  // loads) splits stay at 16 pages or less: wavefronts running side by side
-  // then read a shared prefix's pages close together in time, from L2 (B64
-  // with a shared prefix: 256 tokens 1.7% faster than 1024).
+  // Candidates from the longest split down to the page size; only splits
+  // whose queue holds a task for every resident wavefront qualify; the
+  // cheapest wins, ties to the longer split; none qualifies: the page size.
+  // The fixed cost of a queue position is measured: half a page with
+  // streaming loads, one and a half with cached ones.  Where pages may be
+  // shared (cached loads) splits stay at 16 pages or less: wavefronts
+  // running side by side then read a shared prefix's pages close together
+  // in time, from L2 (B64 with a shared prefix: 256 tokens 4.4% faster than
+  // 1024).
   const bool streaming = (t.flags & KVPAGE_FLAG_STREAM_KV) != 0;
   const int32_t longest = (streaming ? 256 : 16) * t.page_size;
-  int64_t total_pages = 0;
-  for (int b = 0; b < t.B; ++b) total_pages += (ctx_lens_host[b] + t.page_size - 1) / t.page_size;
-  total_pages *= t.Hkv;
-  const int64_t fixed6 = streaming ? 3 : 9;   // six times the fixed cost per position
+  const double fixed = streaming ? 0.5 : 1.5;
   int32_t best = 0;
-  int64_t best_cost = INT64_MAX;
+  double best_cost = 0.0;
   for (int32_t split = longest; split >= t.page_size; split /= 2) {
-    int64_t tasks = 0;
-    for (int b = 0; b < t.B; ++b) tasks += (ctx_lens_host[b] + split - 1) / split;
-    tasks *= t.Hkv;
-    if (tasks < waves) continue;
-    const int64_t chunk_max = split_attn_chunk_max(split);
-    const int64_t rounds = (tasks + waves * chunk_max - 1) / (waves * chunk_max);
-    const int64_t c = (tasks + waves * rounds - 1) / (waves * rounds);
-    const int64_t n = c * rounds;                          // positions on the busiest wavefront
-    const int64_t busiest = n * (split / t.page_size);     // its pages, at most
-    // Six times `waves` times the cost in pages.
-    const int64_t cost = std::max(6 * total_pages, 4 * waves * busiest) + fixed6 * waves * n;
-    if (cost < best_cost) {
+    const double cost = split_cost(t, ctx_lens_host, split, waves, fixed);
+    if (cost < 0.0) continue;
+    if (best == 0 || cost < best_cost) {
       best_cost = cost;
       best = split;
     }

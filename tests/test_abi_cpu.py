@@ -132,11 +132,12 @@ def test_status_strings():
 
 def test_choose_split_fills_the_resident_wavefronts():
     """Among the splits whose queue has a task per resident wavefront
-    (Hkv * sum ceil(ctx / S) >= W), the least cost: the larger of the mean
-    pages per wavefront and the busiest wavefront's pages over 1.5, plus a
-    fixed cost per position; the page size if none qualifies, 256 for an
-    all-empty batch.  Pure host arithmetic with W given (cases worked by
-    hand)."""
+    (Hkv * sum ceil(ctx / S) >= W), the least simulated time: each
+    wavefront's pages plus a fixed cost per queue position under the
+    kernel's schedule, finished by water filling (every unfinished
+    wavefront streams at min(1.43, W / unfinished) pages per unit); the page
+    size if none qualifies, 256 for an all-empty batch.  Pure host
+    arithmetic with W given."""
     def pick(ctx, W=1024, **kw):
         return K.kvpage_choose_split(_shape(B=len(ctx), **kw), ctx, W)
     assert pick([32768]) == 256          # 8 * 128 tasks = 1024
@@ -153,23 +154,31 @@ def test_choose_split_fills_the_resident_wavefronts():
     assert pick([16384], Hq=16, Hkv=4) == 64   # half the KV heads, half the tasks
     for S in (16, 32, 64, 128, 256):
         assert pick([8192] * 3, W=3 * 8 * 8192 // S) >= S
-    # Four sequences of 53248 tokens (13312 pages over 1024 wavefronts: 104
-    # each).  Streaming: 4096 and 2048 leave wavefronts idle (416, 832
-    # tasks); 1024 gives 1664 tasks, two 64-page positions on the busiest
-    # wavefront: max(104, 128 / 1.5) + 2 * 1/2 = 105, against 512 (four
-    # positions: 106), 256 (seven: 107.5).  Cached: at most 256, whose seven
-    # positions cost 104 + 7 * 3/2 = 114.5 against 128's thirteen (123.5).
     stream = K.KVPAGE_FLAG_STREAM_KV
+    # Worked by hand: one KV head, 4 wavefronts (linear schedule), contexts
+    # 2048, 256, 256, 256 tokens (128 + 3 * 16 pages), streaming (1/2 page
+    # per position).  Loads per wavefront, then water filling:
+    #   S = 4096 and 2048: 4 tasks, one each: 128.5, 16.5, 16.5, 16.5
+    #     -> 16.5 + 112 / 1.43 = 94.82
+    #   S = 1024: 5 tasks, chunks of 2: 129, 33, 16.5, 0
+    #     -> 16.5 / (4/3) + 16.5 / 1.43 + 96 / 1.43 = 91.05
+    #   S = 512: 7 tasks, chunks of 2: 65, 65, 33, 16.5
+    #     -> 16.5 + 16.5 / (4/3) + 32 / 1.43 = 51.25
+    #   S = 256: 11 tasks, chunks of 3: 49.5, 49.5, 49.5, 33
+    #     -> 33 + 16.5 / (4/3) = 45.375
+    #   S = 128: 22 tasks, chunks of 6: 51, 51, 51, 34 -> 46.75
+    #   S = 64: 44 tasks, chunks of 11: 49.5 each -> 49.5
+    # so 256.  (Pricing only the busiest wavefront against the mean would take
+    # 512: the many loaded wavefronts of 512 are what water filling sees.)
+    assert pick([2048, 256, 256, 256], W=4, Hq=8, Hkv=1, flags=stream) == 256
+    # Full-size shapes (per-XCD classes: several sequences, Hkv = 8).
+    # Streaming: four 53248-token sequences take 1024 (4096 and 2048 leave
+    # wavefronts idle); cached loads stop at 256.
     assert pick([53248] * 4, max_pages=8192, flags=stream) == 1024
     assert pick([53248] * 4, max_pages=8192) == 256
-    # 73728 tokens each (144 pages per wavefront): 2048 gives 1152 tasks, two
-    # 128-page positions (max(144, 256 / 1.5) + 1 = 171.7); 1024 three of 64
-    # (144 + 1.5); 512 five of 32 (146.5).
     assert pick([73728] * 4, max_pages=8192, flags=stream) == 1024
-    # Chunks of 4096-token tasks hold one position: 8 sequences of 262144
-    # tokens on 2048 wavefronts (512 pages each) give 4096 tasks of 4096, two
-    # rounds of one position (512 + 2 * 1/2); 2048 two rounds of two
-    # (512 + 2), 1024 two of four (512 + 4).
+    # One position per chunk at 4096 tokens: 8 x 262144 tokens on 2048
+    # wavefronts, 4096 tasks in two even rounds.
     assert pick([2097152 // 8] * 8, max_pages=16384, flags=stream, W=2048) == 4096
 
 
@@ -178,7 +187,10 @@ def test_choose_split_on_the_reference_workloads():
     shared), as measured on MI355X against 256-token splits: B8 bimodal and
     B4 bimodal take 1024 (2.3% and 2.8% faster attention), Zipf lengths 2048
     (4.1%), B8 uniform 1024 (no difference measured); one long sequence and
-    the shared-prefix batch keep 256."""
+    the shared-prefix batch keep 256.  The B64 lengths without their shared
+    prefix (private pages, streaming) keep 256 too: measured 366.9 us
+    against 392.0 us at 1024, where many wavefronts carry six 64-page tasks
+    against a mean of 264 pages."""
     from paged_kv_cache_07_amd import workloads as W
     want = {"b1": 256, "b8_bimodal": 1024, "b8_uniform": 1024, "b8_zipf": 2048,
             "b4_bimodal": 1024, "b64_prefix": 256}
@@ -188,6 +200,11 @@ def test_choose_split_on_the_reference_workloads():
         shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, 256, wl.max_pages,
                              wl.num_pages, wl.dtype, wl.scale, flags)
         assert K.kvpage_choose_split(shape, wl.ctx_lens.tolist(), 1024) == split, name
+    wl = W.make("b64_prefix", fill_pools=False)
+    private = (wl.ctx_lens - wl.shared_prefix_pages * wl.page_size).tolist()
+    shape = K.make_shape(wl.B, wl.Hq, wl.Hkv, wl.d, wl.page_size, 256, wl.max_pages,
+                         wl.num_pages, wl.dtype, wl.scale, K.KVPAGE_FLAG_STREAM_KV)
+    assert K.kvpage_choose_split(shape, private, 1024) == 256
 
 
 def test_choose_split_rejects_bad_lengths():

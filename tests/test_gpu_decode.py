@@ -564,16 +564,23 @@ def test_stream_kv_changes_no_bits(case, one_call):
 
 
 @pytest.mark.parametrize("case,split", [("b64_prefix_small", 256), ("b64_prefix_small", 1024),
-                                        ("edge", 256), ("edge", 512), ("edge", 64)])
+                                        ("edge", 256), ("edge", 512), ("edge", 64),
+                                        ("many", 256)])
 def test_shared_prefix_loads_change_no_bits(case, split):
     """KVPAGE_FLAG_STREAM_KV with kvpage_launch_opts.shared_pages: pieces of
     work that start on one of a sequence's shared leading pages load through
     the caches, the rest stream.  Every output is bit-identical to all loads
     cached (same schedule), and matches the oracle.  The edge case gives
     every sequence its own count: none, one page, mid-split, mid-piece, past
-    the end of the context, and the whole table row."""
+    the end of the context, and the whole table row; "many" has 70 sequences,
+    past the fused queue build (separate queue kernel, linear schedule)."""
     from paged_kv_cache_07_amd.device import DecodeStep
-    if case == "edge":
+    if case == "many":
+        rng = np.random.default_rng(34)
+        ctx = rng.integers(0, 3000, size=70).tolist()
+        wl = W.custom(ctx, Hq=16, Hkv=8, d=64, dtype="f16", seed=34, max_pages=200)
+        shared = rng.integers(0, 200, size=70).astype(np.int32)
+    elif case == "edge":
         ctx = [0, 1, 300, 17, 4100, 2048, 9000, 513, 6000, 700, 4096, 15000]
         wl = W.custom(ctx, Hq=16, Hkv=8, d=128, dtype="bf16", seed=33, max_pages=1000)
         shared = np.array([0, 1, 0, 2, 40, 128, 100, 3, 5, 1000, 256, 937], dtype=np.int32)
