@@ -61,6 +61,19 @@ def measured_traffic(config: str):
     return None
 
 
+def workload_title(name, r) -> str:
+    if name == "b1":
+        return "B1 long-context paged GQA decode step"
+    return f"{name} paged GQA decode step ({r['B']} sequences, {r['ctx_total']} tokens)"
+
+
+def kernel_title(r) -> str:
+    loads = ("streaming loads, shared prefix cached" if r["shared_prefix_cached"]
+             else "streaming loads" if r["stream_kv"] else "cached loads")
+    queue = "fused queue" if r["B"] <= 64 else "queue kernel"
+    return f"kvpage::split_attn_kernel<{r['d']}, {r['dtype']}, budget, {queue}, {loads}>"
+
+
 def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = True,
                 stream_kv=None):
     """Time workload `name`: one kvpage_decode_step call per step.
@@ -137,7 +150,8 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
     n_tasks = int(ds.n_tasks.item())
     return {
         "workload": name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d,
-        "page_size": wl.page_size, "split_tokens": wl.split_tokens, "dtype": wl.dtype,
+        "page_size": wl.page_size, "split_tokens": split_tokens or wl.split_tokens,
+        "dtype": wl.dtype, "num_pages": wl.num_pages, "max_ctx": int(wl.ctx_lens.max()),
         "ctx_total": int(wl.ctx_lens.sum()), "n_tasks": n_tasks, "kv_bytes": kv,
         "kv_bytes_unique": W.kv_bytes(wl, unique=True), "stream_kv": stream_kv,
         "shared_prefix_cached": shared is not None,
@@ -475,12 +489,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic: seeded N(0,1) fp16 q/K/V, pages scattered by a seeded permutation",
-        "config": {"workload": "B1 long-context paged GQA decode step", "B": 1, "context": 32768,
-                   "Hq": 32, "Hkv": 8, "d": 128, "page_size": 16, "split_tokens": 256,
-                   "pool_pages": 4096, "budgeting_outputs": True, "cold_cache": flush,
-                   "stream_kv": head["stream_kv"]},
+        "dtype": head["dtype"],
+        "data": f"synthetic: seeded N(0,1) {head['dtype']} q/K/V, pages scattered by a seeded permutation",
+        "config": {"workload": workload_title(args.config, head), "B": head["B"],
+                   "context": head["max_ctx"] if head["B"] == 1 else None,
+                   "tokens": head["ctx_total"], "Hq": head["Hq"], "Hkv": head["Hkv"],
+                   "d": head["d"], "page_size": head["page_size"],
+                   "split_tokens": head["split_tokens"], "pool_pages": head["num_pages"],
+                   "budgeting_outputs": True, "cold_cache": flush,
+                   "stream_kv": head["stream_kv"],
+                   "shared_prefix_cached": head["shared_prefix_cached"]},
         "steps_per_s": 1e3 / head["step_ms_mean"],
         "frac_hbm_peak_step": kv / head["step_ms_mean"] / 1e6 / HBM_PEAK_GBS,
         "step_ms_p50": head["step_ms_p50"], "step_ms_p10": head["step_ms_p10"],
@@ -488,8 +506,7 @@ def main():
         "warm_step_ms_mean": warm["step_ms_mean"], "warm_steps_per_s": 1e3 / warm["step_ms_mean"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "kvpage::split_attn_kernel<128, f16, budget, fused queue"
-                               + (", streaming loads>" if head["stream_kv"] else ">"),
+                     "kernel": kernel_title(head),
                      "attn_ms_mean": head["attn_ms_mean"],
                      "algorithmic_bytes_per_launch": kv},
         "also": also,
