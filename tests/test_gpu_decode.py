@@ -342,13 +342,16 @@ def test_one_call_step_equals_separate_calls(budget):
             compare_step(ra, ref, budget=budget, label=name)
 
 
-@pytest.mark.parametrize("max_wg,split", [(1, 256), (3, 256), (1, 64), (3, 32), (2, 128)])
+@pytest.mark.parametrize("max_wg,split", [(1, 256), (3, 256), (1, 64), (3, 32), (2, 128),
+                                          (8, 256), (16, 64), (8, 1024)])
 def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
     """Few workgroups: each wavefront walks a long stretch of the queue,
     folding consecutive tasks of one (sequence, KV head) into one partial and
     crossing group boundaries inside its stretch.  Splits shorter than 16
     pages put several short tasks in one run, whose staged page values must
-    land on the right logical pages."""
+    land on the right logical pages.  With 8 or 16 workgroups the one-call
+    step of the Hkv = 8 batches runs one class of KV heads per XCD, so run
+    starts sit at class-chunk offsets the merge must recompute."""
     from paged_kv_cache_07_amd import binding
     from paged_kv_cache_07_amd.device import DecodeStep
     cases = [W.make("b8_bimodal", ctx_divisor=32), W.make("b64_prefix", ctx_divisor=16),
@@ -361,6 +364,8 @@ def test_long_wave_runs_fold_consecutive_tasks(max_wg, split):
             ds = DecodeStep(wl, budget=budget, split_tokens=split)
             ds.step(opts=binding.make_opts(max_workgroups=max_wg))
             res = ds.results()
+            classes = 8 if (max_wg % 8 == 0 and wl.B >= 2 and wl.Hkv % 8 == 0) else 1
+            assert ds.schedule_classes() == classes, (wl.name, max_wg)
             compare_step(res, oracle_step(wl, split_tokens=split), budget=budget,
                          label=f"{wl.name} wg{max_wg} S{split}")
 
