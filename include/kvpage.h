@@ -221,7 +221,9 @@ int kvpage_decode_attn(const kvpage_shape* shape, const void* q, const void* k_p
  *     records at its start and end (NULL: none).
  *   max_workgroups: cap on the attention kernel's persistent grid (0: as many
  *     as are resident on the device).  Fewer workgroups give each wavefront a
- *     longer contiguous stretch of the queue; results do not depend on it.
+ *     longer contiguous stretch of the queue, which it folds into fewer run
+ *     partials: results agree to rounding whatever the cap, the bits of out,
+ *     lse and page mass depend on it.
  *   shared_pages: NULL, or DEVICE int32 [B]: the first shared_pages[b] logical
  *     pages of sequence b's table row may also be referenced by other
  *     sequences (a shared prompt prefix, as prefix caching keeps it; GrowPage,
@@ -243,8 +245,12 @@ typedef struct {
  * (as kvpage_merge_splits); with `budget` the merge also finishes the
  * budgeting outputs exactly as kvpage_page_mass would, in the same kernel.
  * Outputs equal those of kvpage_build_queue + kvpage_decode_attn (+
- * kvpage_page_mass).  tasks, group_offsets and n_tasks are written.
- * opts may be NULL. */
+ * kvpage_page_mass): the queue, page maxima and summaries bit for bit; out,
+ * lse and page mass bit for bit as well when B == 1, B > 64 or Hkv is not a
+ * multiple of 8, and to rounding otherwise (there the attention kernel runs
+ * each KV head's tasks on one XCD and so folds them into different runs).
+ * Repeated calls with the same inputs and opts give the same bits.
+ * tasks, group_offsets and n_tasks are written.  opts may be NULL. */
 int kvpage_decode_step(const kvpage_shape* shape, const void* q, const void* k_pool,
                        const void* v_pool, const int32_t* block_tables, const int32_t* ctx_lens,
                        kvpage_task* tasks, int32_t* group_offsets, int32_t* n_tasks,
