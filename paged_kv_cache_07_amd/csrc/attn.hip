@@ -448,15 +448,15 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         float acc = hv[0][x];
 #pragma unroll
         for (int h = 1; h < kMaxG; ++h)
-          if (h < G) acc = __fadd_rn(acc, hv[h][x]);
-        const float qbar = __fmul_rn(acc, p.inv_g);
+          if (h < G) acc = add_rn(acc, hv[h][x]);
+        const float qbar = mul_rn(acc, p.inv_g);
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
           float rem = ema_step(sv[which][x], qbar, which ? p.alpha_slow : p.alpha_fast);
 #pragma unroll
           for (int piece = 0; piece < NPC; ++piece) {
             pcs[which][piece][x] = E::bits(rem);
-            rem = __fsub_rn(rem, E::value(pcs[which][piece][x]));
+            rem = sub_rn(rem, E::value(pcs[which][piece][x]));
           }
         }
       }
@@ -623,8 +623,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           // Summary pieces sit in adjacent columns: add them into the lead column.
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float sum = __fadd_rn(acc[e], from_right<1>(acc[e]));
-            if constexpr (NPC == 3) sum = __fadd_rn(sum, from_right<2>(acc[e]));
+            float sum = add_rn(acc[e], from_right<1>(acc[e]));
+            if constexpr (NPC == 3) sum = add_rn(sum, from_right<2>(acc[e]));
             acc[e] = is_head ? acc[e] : sum;
           }
         }
@@ -747,7 +747,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         if constexpr (BF) {
           uint32_t rb[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rb[e] = E::bits(__fsub_rn(pe[e], E::value(pb[e])));
+          for (int e = 0; e < 4; ++e) rb[e] = E::bits(sub_rn(pe[e], E::value(pb[e])));
           pop_lo[0] = rb[0] | (rb[1] << 16);
           pop_lo[1] = rb[2] | (rb[3] << 16);
         }
@@ -876,8 +876,12 @@ template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, int LOAD
 static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop, int max_wg) {
   auto kern = split_attn_kernel<D, BF, BUDGET, DEPTH, FUSEDQ, PPT, LOADS>;
-  // Resident workgroups of this instance per device, found once.  Concurrent
-  // first calls may both look it up; they store the same value.
+  // The grid is one workgroup per compute unit, whatever else would fit:
+  // the grid, and with it the schedule, the runs and the rounding of every
+  // result, is then the same for every instance (the load policies give the
+  // same bits); a second resident workgroup measured no faster.  Compute
+  // units per device, found once; concurrent first calls store the same
+  // value.
   static std::atomic<int> resident_wg[64];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
@@ -888,10 +892,7 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
     int cus = 0;
     err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
-    int per = 0;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kWave * kWavesPerGroup, 0);
-    if (err != hipSuccess) return err;
-    resident_n = (per > 0 ? per : 1) * cus;
+    resident_n = cus > 0 ? cus : 1;
     cached.store(resident_n, std::memory_order_relaxed);
   }
   const int64_t want = ((int64_t)capacity + kWavesPerGroup - 1) / kWavesPerGroup;

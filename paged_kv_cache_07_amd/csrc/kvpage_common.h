@@ -14,7 +14,19 @@
 
 #include "kvpage.h"
 
+// No product is fused into a following sum anywhere after this point (in
+// every source that includes this header): each multiply and add rounds on
+// its own, explicit fmaf excepted, so two instances of one kernel (or two
+// copies of a body inside one) compute the same bits.
+#pragma clang fp contract(off)
+
 namespace kvpage {
+
+// Separately rounded float operations (HIP's __fadd_rn and friends are plain
+// operators compiled where they are defined, which lets them fuse).
+__device__ __forceinline__ float add_rn(float a, float b) { return a + b; }
+__device__ __forceinline__ float sub_rn(float a, float b) { return a - b; }
+__device__ __forceinline__ float mul_rn(float a, float b) { return a * b; }
 
 constexpr int kPage = 16;   // tokens per page: the M dimension of a 16x16 MFMA tile
 constexpr int kWave = 64;   // CDNA wavefront width
@@ -84,15 +96,15 @@ __device__ __forceinline__ uint32_t div_by(uint32_t n, DivMagic dm) {
 template <typename LoadQ>
 __device__ __forceinline__ float group_mean(LoadQ load_q, int G, float inv_g) {
   float s = load_q(0);
-  for (int h = 1; h < G; ++h) s = __fadd_rn(s, load_q(h));
-  return __fmul_rn(s, inv_g);
+  for (int h = 1; h < G; ++h) s = add_rn(s, load_q(h));
+  return mul_rn(s, inv_g);
 }
 
 // One exponential-moving-average step of a query summary (GrowPage:
 // dual-timescale query summaries): s <- (1 - a) * s + a * qbar, rounded
 // step by step (no contraction) so that every kernel agrees bitwise.
 __device__ __forceinline__ float ema_step(float s_prev, float qbar, float a) {
-  return __fadd_rn(__fmul_rn(__fsub_rn(1.0f, a), s_prev), __fmul_rn(a, qbar));
+  return add_rn(mul_rn(sub_rn(1.0f, a), s_prev), mul_rn(a, qbar));
 }
 
 // Workspace.  A header word holds the chunk length c the attention kernel

@@ -352,8 +352,8 @@ struct SummaryStep {
       float acc = bits_value<BF>((qb[0] >> (16 * e)) & 0xffffu);
 #pragma unroll
       for (int hq = 1; hq < kMaxGroup; ++hq)
-        if (hq < p.G) acc = __fadd_rn(acc, bits_value<BF>((qb[hq] >> (16 * e)) & 0xffffu));
-      const float qbar = __fmul_rn(acc, f.inv_g);
+        if (hq < p.G) acc = add_rn(acc, bits_value<BF>((qb[hq] >> (16 * e)) & 0xffffu));
+      const float qbar = mul_rn(acc, f.inv_g);
       f.s_next[si[0] + e] = ema_step(sp[0][e], qbar, f.alpha_fast);
       f.s_next[si[1] + e] = ema_step(sp[1][e], qbar, f.alpha_slow);
     }
