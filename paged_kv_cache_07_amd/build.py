@@ -24,6 +24,15 @@ SOURCES = ("api.hip", "queue.hip", "attn.hip", "merge.hip", "append.hip", "check
            "decide.hip")
 ARCH = "gfx950"
 
+# Leading kernel arguments preloaded into SGPRs at wave launch (gfx950), per
+# source: each kernel's first loads then need no kernel-argument load before
+# them.  The attention kernel's first-load buffers and B (3 arguments), the
+# merge/finish kernels' row-metadata buffers and shape fields (9), the queue
+# kernel's lengths and scan fields (5), the append kernel's lengths, free
+# count, B and max_pages (4).  The compiler also emits the kernel-argument
+# loads in a prologue that firmware without preloading runs instead.
+PRELOAD_ARGS = {"attn.hip": 3, "merge.hip": 9, "queue.hip": 5, "append.hip": 4}
+
 # The packed-FP32 feature is switched off: every float op stays scalar.
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -55,7 +64,9 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        out = _run([cc, *flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        pre = PRELOAD_ARGS.get(src)
+        extra = ["-mllvm", f"-amdgpu-kernarg-preload-count={pre}"] if pre else []
+        out = _run([cc, *flags, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         return obj, out
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:

@@ -41,27 +41,32 @@ __device__ __forceinline__ int page_of(const AppendParams& p, int i, int t, int 
 // Sequence 0's wavefront goes over every sequence: it writes the new free
 // count and the status word (row full, free list exhausted, page id outside
 // the pool).  The lengths are read from ctx_in and written to ctx_out, so no
-// wavefront sees another's update.
-__global__ void __launch_bounds__(kWave) append_kernel(const AppendParams p) {
+// wavefront sees another's update.  The buffers of the first loads (lengths,
+// free count), B and max_pages come first as arguments of their own, which
+// gfx950 can preload into SGPRs at wave launch.
+__global__ void __launch_bounds__(kWave) append_kernel(const int32_t* lead_ctx,
+                                                       const int32_t* lead_fc, int32_t lead_b,
+                                                       int32_t lead_max_pages,
+                                                       const AppendParams p) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const int max_ctx = p.max_pages * kPage;
-  const int fc = p.free_count_in[0];
-  const int scan_end = b == 0 ? p.B : b;
+  const int max_ctx = lead_max_pages * kPage;
+  const int fc = lead_fc[0];
+  const int scan_end = b == 0 ? lead_b : b;
   int before = 0;   // sequences before b needing a page (all of them, for b = 0)
   int flags = 0;
   for (int base = 0; base < scan_end; base += kWave) {
     const int i = base + lane;
-    const int t = i < p.B ? p.ctx_in[i] : 0;
-    const bool need = i < p.B && t >= 0 && t < max_ctx && t % kPage == 0;
+    const int t = i < lead_b ? lead_ctx[i] : 0;
+    const bool need = i < lead_b && t >= 0 && t < max_ctx && t % kPage == 0;
     const uint64_t m = __builtin_amdgcn_ballot_w64(need);
     if (b == 0) {
       const int k = before + (int)__builtin_amdgcn_mbcnt_hi(
           (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const int pg = i < p.B ? page_of(p, i, t, k, fc, max_ctx) : 0;
-      const bool full = i < p.B && (t < 0 || t >= max_ctx);
+      const int pg = i < lead_b ? page_of(p, i, t, k, fc, max_ctx) : 0;
+      const bool full = i < lead_b && (t < 0 || t >= max_ctx);
       const bool starved = need && k >= fc;
-      const bool bad = i < p.B && !full && !starved && (pg < 0 || pg >= p.num_pages);
+      const bool bad = i < lead_b && !full && !starved && (pg < 0 || pg >= p.num_pages);
       if (__builtin_amdgcn_ballot_w64(full)) flags |= KVPAGE_APPEND_FULL;
       if (__builtin_amdgcn_ballot_w64(starved)) flags |= KVPAGE_APPEND_NO_PAGE;
       if (__builtin_amdgcn_ballot_w64(bad)) flags |= KVPAGE_APPEND_BAD_PAGE;
@@ -79,7 +84,7 @@ __global__ void __launch_bounds__(kWave) append_kernel(const AppendParams p) {
     }
     before = 0;
   }
-  const int t = p.ctx_in[b];
+  const int t = lead_ctx[b];
   const int page = page_of(p, b, t, before, fc, max_ctx);
   const bool ok = page >= 0 && page < p.num_pages;
   if (ok) {
@@ -124,7 +129,8 @@ hipError_t launch_append(const kvpage_shape& s, const void* k_new, const void* v
   p.d = s.d;
   p.max_pages = s.max_pages;
   p.num_pages = s.num_pages;
-  hipLaunchKernelGGL(append_kernel, dim3(s.B), dim3(kWave), 0, stream, p);
+  hipLaunchKernelGGL(append_kernel, dim3(s.B), dim3(kWave), 0, stream, p.ctx_in, p.free_count_in,
+                     p.B, p.max_pages, p);
   return hipGetLastError();
 }
 

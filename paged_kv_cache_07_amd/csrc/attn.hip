@@ -218,9 +218,14 @@ __device__ __forceinline__ SeqScan scan_lengths(int32_t raw, int B, int Hkv, int
   return q;
 }
 
+// The buffers of a wavefront's first dependent load (the lengths, or the
+// caller's task count) and B come first, as arguments of their own: gfx950
+// can preload leading scalar kernel arguments into SGPRs at wave launch, so
+// that load does not wait for the kernel-argument block.
 template <int D, bool BF, bool BUDGET, int DEPTH, bool FUSEDQ, int PPT, int LOADS>
 __global__ void __launch_bounds__(kWave * kWavesPerGroup)
-    split_attn_kernel(const AttnParams p) {
+    split_attn_kernel(const int32_t* lead_lens, const int32_t* lead_ntasks, int32_t lead_B,
+                      const AttnParams p) {
   using E = Elem<BF>;
   constexpr int KB = D / 32;   // 16x16x32 MFMAs per page for the scores
   constexpr int VD = D / 16;   // output column blocks; V halves per lane per token
@@ -487,7 +492,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
   u32x4 qop[KB];
   int ntask;
   if constexpr (FUSEDQ) {
-    const int32_t raw_len = load_length(p.ctx_lens, p.B, lane);
+    const int32_t raw_len = load_length(lead_lens, lead_B, lane);
     sq = scan_lengths(raw_len, p.B, p.Hkv, p.split_tokens, p.div_split, p.max_pages, lane);
     ntask = min(sq.total, p.capacity);
     if (blockIdx.x == 0 && wave == 0) {
@@ -502,7 +507,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       }
     }
   } else {
-    ntask = min(p.n_tasks[0], p.capacity);
+    ntask = min(lead_ntasks[0], p.capacity);
   }
   // Classes: with ncls > 1 the queue is taken as ncls classes, class x the
   // (sequence, KV head) groups with g % ncls == x in queue order, and class x
@@ -912,9 +917,10 @@ static hipError_t launch_one(const AttnParams& p, int capacity, hipStream_t stre
   if (ev_start || ev_stop) {
     // Timestamps taken by the dispatch itself: start and end of this kernel.
     hipExtLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, ev_start,
-                          ev_stop, 0, a);
+                          ev_stop, 0, a.ctx_lens, a.n_tasks, a.B, a);
   } else {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWave * kWavesPerGroup), 0, stream, a.ctx_lens,
+                       a.n_tasks, a.B, a);
   }
   return hipGetLastError();
 }

@@ -104,19 +104,38 @@ struct Row {
   int b, h, g, hh, lo, n, runlen, off, nrun, npg;
 };
 
-__device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pages) {
+// The buffers of the row metadata loads and the shape fields their addresses
+// need.  The merge and finish kernels take these as leading kernel arguments
+// of their own (KV_ROW_LEAD_ARGS): gfx950 can preload leading scalar kernel
+// arguments into SGPRs at wave launch, so a workgroup's first loads do not
+// wait for the kernel-argument block.
+struct RowLead {
+  const int32_t* group_offsets;
+  const int32_t* ws_hdr;
+  const int32_t* ctx_lens;
+  int32_t B, Hq, Hkv, G;
+};
+#define KV_ROW_LEAD_ARGS                                                               \
+  const int32_t *lead_go, const int32_t *lead_hdr, const int32_t *lead_ctx, int32_t lead_b, \
+      int32_t lead_hq, int32_t lead_hkv, int32_t lead_g
+#define KV_ROW_LEAD RowLead{lead_go, lead_hdr, lead_ctx, lead_b, lead_hq, lead_hkv, lead_g}
+#define KV_ROW_LEAD_OF(p) \
+  (p).group_offsets, (p).ws_hdr, (p).fin.ctx_lens, (p).B, (p).Hq, (p).Hkv, (p).G
+
+__device__ __forceinline__ Row row_of(const MergeParams& p, const RowLead& ld, int bh,
+                                      bool need_pages) {
   Row r;
-  r.b = bh / p.Hq;
-  r.h = bh % p.Hq;
-  r.g = r.h / p.G;
-  r.hh = r.h % p.G;
-  const int lo = p.group_offsets[r.b * p.Hkv + r.g];
-  const int hi = p.group_offsets[r.b * p.Hkv + r.g + 1];
-  const int runlen = p.ws_hdr[0];
-  const int ncls = p.ws_hdr[1];
-  const int seq_lo = p.group_offsets[r.b * p.Hkv];
-  const int seq_lo1 = p.group_offsets[r.b * p.Hkv + 1];
-  const int ctx = need_pages ? clamp_ctx(p.fin.ctx_lens[r.b], p.fin.max_pages) : 0;
+  r.b = bh / ld.Hq;
+  r.h = bh % ld.Hq;
+  r.g = r.h / ld.G;
+  r.hh = r.h % ld.G;
+  const int lo = ld.group_offsets[r.b * ld.Hkv + r.g];
+  const int hi = ld.group_offsets[r.b * ld.Hkv + r.g + 1];
+  const int runlen = ld.ws_hdr[0];
+  const int ncls = ld.ws_hdr[1];
+  const int seq_lo = ld.group_offsets[r.b * ld.Hkv];
+  const int seq_lo1 = ld.group_offsets[r.b * ld.Hkv + 1];
+  const int ctx = need_pages ? clamp_ctx(ld.ctx_lens[r.b], p.fin.max_pages) : 0;
   r.lo = min(max(lo, 0), p.capacity);
   r.n = max(min(hi, p.capacity) - r.lo, 0);
   r.runlen = max(1, runlen);
@@ -124,7 +143,7 @@ __device__ __forceinline__ Row row_of(const MergeParams& p, int bh, bool need_pa
   // the queue taken as ncls classes (KV heads g % ncls), class-local position
   // of the group's first task: start / ncls + (g / ncls) * ns for the
   // sequence's first queue position `start` and ns tasks per KV head.
-  if (ncls > 1 && p.Hkv % ncls == 0) {
+  if (ncls > 1 && ld.Hkv % ncls == 0) {
     const int start = max(seq_lo, 0);
     const int ns = max(seq_lo1 - start, 0);
     r.off = (start / ncls + (r.g / ncls) * ns) % r.runlen;
@@ -367,11 +386,11 @@ struct SummaryStep {
 // loads its neighbour's, which stay in cache), so the data arrives in one
 // memory round trip and the compiler's wait counts stay exact.
 template <int D, bool BF, bool FINISH, int CG>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const MergeParams p, int nslice,
-                                                              int nsub) {
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(KV_ROW_LEAD_ARGS, int nslice,
+                                                              int nsub, const MergeParams p) {
   __shared__ float scratch[2 * kMergeThreads / kWave];
   const int bh = blockIdx.x / nsub, sub = blockIdx.x % nsub;
-  const Row r = row_of(p, bh, FINISH);
+  const Row r = row_of(p, KV_ROW_LEAD, bh, FINISH);
   const bool do_cols = sub < CG;
   const bool do_pages = FINISH && sub < nslice;
   const int col0 = min(sub, CG - 1) * (D / CG);
@@ -418,13 +437,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <int D, bool BF, bool FINISH>
-__global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergeParams p, int nslice) {
+__global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(KV_ROW_LEAD_ARGS, int nslice,
+                                                                   const MergeParams p) {
   constexpr int CPL = D / kWave;   // output columns per lane (1 or 2)
   const int lane = threadIdx.x & (kWave - 1);
   const int item = blockIdx.x * (kMergeThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (item >= p.B * p.Hq * nslice) return;
+  if (item >= lead_b * lead_hq * nslice) return;
   const int bh = item / nslice, slice = item % nslice;
-  const Row r = row_of(p, bh, FINISH);
+  const Row r = row_of(p, KV_ROW_LEAD, bh, FINISH);
   const bool do_out = slice == 0;
 
   // Run partials of this lane's columns, first batch.
@@ -525,9 +545,10 @@ __global__ void __launch_bounds__(kMergeThreads) merge_wave_kernel(const MergePa
 // Standalone finish after a merge that already wrote lse: one workgroup per
 // slice of pages of one row.
 template <bool BF>
-__global__ void __launch_bounds__(kMergeThreads) finish_kernel(const MergeParams p, int D, int nslice) {
+__global__ void __launch_bounds__(kMergeThreads) finish_kernel(KV_ROW_LEAD_ARGS, int nslice,
+                                                               const MergeParams p, int D) {
   const int bh = blockIdx.x / nslice, slice = blockIdx.x % nslice;
-  const Row r = row_of(p, bh, true);
+  const Row r = row_of(p, KV_ROW_LEAD, bh, true);
   PageLoads pl;
   pl.issue(p, r, bh, slice);
   finish_slice<BF>(p, r, bh, slice, D, pl, p.lse[bh]);
@@ -584,12 +605,12 @@ static void launch_merge_d(int rows, int nslice, const MergeParams& p, hipStream
   if (rows < kWaveMergeMinRows) {
     const int nsub = nslice > 4 ? nslice : 4;
     hipLaunchKernelGGL((merge_kernel<D, BF, FINISH, 4>), dim3(rows * nsub), dim3(kMergeThreads), 0,
-                       stream, p, nslice, nsub);
+                       stream, KV_ROW_LEAD_OF(p), nslice, nsub, p);
   } else {
     const int waves_per_block = kMergeThreads / kWave;
     const int grid = (rows * nslice + waves_per_block - 1) / waves_per_block;
     hipLaunchKernelGGL((merge_wave_kernel<D, BF, FINISH>), dim3(grid), dim3(kMergeThreads), 0,
-                       stream, p, nslice);
+                       stream, KV_ROW_LEAD_OF(p), nslice, p);
   }
 }
 
@@ -637,9 +658,11 @@ hipError_t launch_page_mass(const kvpage_shape& s, const kvpage_budget& bud, con
   const int nslice = page_slices(s);
   const int grid = s.B * s.Hq * nslice;
   if (s.dtype == KVPAGE_BF16)
-    hipLaunchKernelGGL(finish_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d, nslice);
+    hipLaunchKernelGGL(finish_kernel<true>, dim3(grid), dim3(kMergeThreads), 0, stream,
+                       KV_ROW_LEAD_OF(p), nslice, p, s.d);
   else
-    hipLaunchKernelGGL(finish_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, stream, p, s.d, nslice);
+    hipLaunchKernelGGL(finish_kernel<false>, dim3(grid), dim3(kMergeThreads), 0, stream,
+                       KV_ROW_LEAD_OF(p), nslice, p, s.d);
   return hipGetLastError();
 }
 
