@@ -176,10 +176,29 @@ constexpr int kLoadsCached = 0;
 constexpr int kLoadsStream = 1;
 constexpr int kLoadsPrefix = 2;
 
+// Run outputs (partials, page values) go past the L2 in the prefix-aware
+// instances, where they would otherwise evict the shared prefix pages each
+// XCD's L2 holds.  Measured on MI355X in alternating processes: B64 with a
+// 128-page shared prefix 364.3 -> 357.6 us.  With streaming loads and no
+// sharing they stay ordinary stores: B8 bimodal 132.0 -> 133.6 us with them
+// streamed, B1 -0.2 us in one comparison and unchanged in another.
+template <int LOADS>
+struct OutPolicy {
+  static constexpr bool kStream = LOADS == kLoadsPrefix;
+};
+
 template <bool STREAM, typename V>
 __device__ __forceinline__ V tile_load(const char* addr) {
   if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const V*>(addr));
   else return *reinterpret_cast<const V*>(addr);
+}
+
+// A run output store: non-temporal with STREAM, so the value goes past the
+// L2 instead of staying there dirty.
+template <bool STREAM, typename T>
+__device__ __forceinline__ void out_store(T* addr, T v) {
+  if constexpr (STREAM) __builtin_nontemporal_store(v, addr);
+  else *addr = v;
 }
 
 struct SeqScan {
@@ -227,6 +246,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
     split_attn_kernel(const int32_t* lead_lens, const int32_t* lead_ntasks, int32_t lead_B,
                       const AttnParams p) {
   using E = Elem<BF>;
+  constexpr bool NTO = OutPolicy<LOADS>::kStream;   // run outputs past the L2
   constexpr int KB = D / 32;   // 16x16x32 MFMAs per page for the scores
   constexpr int VD = D / 16;   // output column blocks; V halves per lane per token
   constexpr int VW = VD / 2;   // V dwords per lane per token
@@ -795,8 +815,8 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
       __builtin_amdgcn_s_setprio(3);
       const float ltot = rows_sum(l);
       if (r == 0 && is_head) {
-        p.ws_rm[(int64_t)run_start * G + n] = mrun;
-        p.ws_rl[(int64_t)run_start * G + n] = ltot;
+        out_store<NTO>(&p.ws_rm[(int64_t)run_start * G + n], mrun);
+        out_store<NTO>(&p.ws_rl[(int64_t)run_start * G + n], ltot);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -804,7 +824,7 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         if (h < G) {
           float* dst = p.ws_o + ((int64_t)run_start * G + h) * D + n * VD;
 #pragma unroll
-          for (int j = 0; j < VD; ++j) dst[j] = O[j][e];
+          for (int j = 0; j < VD; ++j) out_store<NTO>(&dst[j], O[j][e]);
         }
       }
       const int nk = ktask + 1;
@@ -824,12 +844,14 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
         for (int hb = 0; hb < kMaxG; hb += 4) {
           const int h = hb + hl;
           if (hb < G && h < G && pg < npg)
-            p.page_mass[((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0 + pg] =
-                lds_mass[wave][0][h][pg];
+            out_store<NTO>(
+                &p.page_mass[((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0 + pg],
+                lds_mass[wave][0][h][pg]);
         }
         if (hl < 2 && pg < npg)
-          p.page_max[(((int64_t)hl * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0 + pg] =
-              lds_pmax[wave][0][hl][pg];
+          out_store<NTO>(
+              &p.page_max[(((int64_t)hl * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0 + pg],
+              lds_pmax[wave][0][hl][pg]);
       } else if constexpr (BUDGET) {
         // Raw page sums move to the run's final reference, the one its
         // partial carries; pages of a run are consecutive in the sequence.
@@ -840,15 +862,15 @@ __global__ void __launch_bounds__(kWave * kWavesPerGroup)
           float* row = p.page_mass + ((int64_t)b * p.Hq + (int64_t)g * G + h) * p.max_pages + run_lp0;
           for (int pp = lane; pp < rp; pp += kWave) {
             const int kk = pp / upg;   // piece of the run holding page pp
-            row[pp] = lds_mass[wave][kk][h][pp - kk * upg] *
-                      __builtin_amdgcn_exp2f(lds_tref[wave][kk][h] - mh);
+            out_store<NTO>(&row[pp], lds_mass[wave][kk][h][pp - kk * upg] *
+                                         __builtin_amdgcn_exp2f(lds_tref[wave][kk][h] - mh));
           }
         }
         for (int which = 0; which < 2; ++which) {
           float* row = p.page_max + (((int64_t)which * p.B + b) * p.Hkv + g) * p.max_pages + run_lp0;
           for (int pp = lane; pp < rp; pp += kWave) {
             const int kk = pp / upg;
-            row[pp] = lds_pmax[wave][kk][which][pp - kk * upg];
+            out_store<NTO>(&row[pp], lds_pmax[wave][kk][which][pp - kk * upg]);
           }
         }
       }
