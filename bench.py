@@ -74,6 +74,39 @@ def kernel_title(r) -> str:
     return f"kvpage::split_attn_kernel<{r['d']}, {r['dtype']}, budget, {queue}, {loads}>"
 
 
+_SPIN_CYCLES_PER_MS = None
+
+
+def hold_stream(ms: float):
+    """Keep the launch stream busy for about `ms` milliseconds (a device-side
+    spin) while the host enqueues a timed loop behind it.  The per-step
+    events then see the device's time only: a host slower to launch than the
+    device is to run never shows up as gaps between the timed steps.  The
+    spin's clock rate is calibrated once with events."""
+    import torch
+
+    from paged_kv_cache_07_amd import binding
+
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        a, b = binding.HipEvent(), binding.HipEvent()
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = 2_000_000 / max(a.elapsed_ms(b), 1e-3)
+    torch.cuda._sleep(int(min(ms, 500.0) * _SPIN_CYCLES_PER_MS))
+
+
+def host_ms_per_iter(fn, iters: int) -> float:
+    """Host time to enqueue one iteration of `fn` (no synchronisation)."""
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        fn()
+    return (time.perf_counter() - t0) * 1e3 / max(iters, 1)
+
+
 def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = True,
                 stream_kv=None):
     """Time workload `name`: one kvpage_decode_step call per step.
@@ -120,14 +153,18 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
         if flush:
             torch.sum(flush_buf, dim=0, out=sink[0])
 
-    for _ in range(warmup):
+    def one():
         flush_caches()
         ds.step()
+
+    host_ms = host_ms_per_iter(one, max(warmup, 1))
     torch.cuda.synchronize()
 
-    # Region 1: whole steps.
+    # Region 1: whole steps, enqueued behind a spin that outlasts the host's
+    # launches.
     ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
+    hold_stream(2.0 * steps * host_ms + 2.0)
     t0 = time.perf_counter()
     for a, b in ev:
         flush_caches()
@@ -158,7 +195,7 @@ def time_config(name: str, steps: int, warmup: int, flush: bool, budget: bool = 
         "step_ms_mean": float(step_ms.mean()), "step_ms_p50": float(np.median(step_ms)),
         "step_ms_p10": float(np.percentile(step_ms, 10)), "step_ms_p90": float(np.percentile(step_ms, 90)),
         "attn_ms_mean": float(attn_ms.mean()), "attn_ms_p50": float(np.median(attn_ms)),
-        "wall_s": wall, "cold_cache": flush,
+        "wall_s": wall, "cold_cache": flush, "host_enqueue_ms_per_step": host_ms,
     }
 
 
@@ -187,6 +224,8 @@ def time_append(name: str, calls: int, flush: bool):
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
     ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(calls + 3)]
+    torch.cuda.synchronize()
+    hold_stream(2.0 * len(ev) * 0.5 + 2.0)   # ~0.5 ms of host work per call at most
     for a, b in ev:       # the first three calls are warm-up
         if flush:
             torch.sum(flush_buf, dim=0, out=sink[0])
@@ -228,6 +267,8 @@ def time_decide(name: str, calls: int, flush: bool, tau: float = 0.9):
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
     ev = [(binding.HipEvent(), binding.HipEvent()) for _ in range(calls + 3)]
+    torch.cuda.synchronize()
+    hold_stream(2.0 * len(ev) * 0.5 + 2.0)
     for a, b in ev:       # the first three calls are warm-up
         if flush:
             torch.sum(flush_buf, dim=0, out=sink[0])
@@ -503,6 +544,7 @@ def main():
         "frac_hbm_peak_step": kv / head["step_ms_mean"] / 1e6 / HBM_PEAK_GBS,
         "step_ms_p50": head["step_ms_p50"], "step_ms_p10": head["step_ms_p10"],
         "step_ms_p90": head["step_ms_p90"], "n_tasks": head["n_tasks"], "kv_bytes": kv,
+        "host_enqueue_ms_per_step": head["host_enqueue_ms_per_step"],
         "warm_step_ms_mean": warm["step_ms_mean"], "warm_steps_per_s": 1e3 / warm["step_ms_mean"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
