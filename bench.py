@@ -88,15 +88,19 @@ def hold_stream(ms: float):
     from paged_kv_cache_07_amd import binding
 
     global _SPIN_CYCLES_PER_MS
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is None:   # no device spin in this torch: the loop runs unheld
+        return
     if _SPIN_CYCLES_PER_MS is None:
+        spin(1000)     # first launch (code load) outside the calibration
         a, b = binding.HipEvent(), binding.HipEvent()
         torch.cuda.synchronize()
         a.record()
-        torch.cuda._sleep(2_000_000)
+        spin(2_000_000)
         b.record()
         torch.cuda.synchronize()
         _SPIN_CYCLES_PER_MS = 2_000_000 / max(a.elapsed_ms(b), 1e-3)
-    torch.cuda._sleep(int(min(ms, 500.0) * _SPIN_CYCLES_PER_MS))
+    spin(int(min(ms, 500.0) * _SPIN_CYCLES_PER_MS))
 
 
 def host_ms_per_iter(fn, iters: int) -> float:
