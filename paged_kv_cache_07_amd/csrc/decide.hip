@@ -68,21 +68,48 @@ __device__ __forceinline__ uint64_t fixed_weight(float x, float M) {
 
 __device__ __forceinline__ int pages_in(int32_t ctx) { return (ctx + kPage - 1) / kPage; }
 
-// Workgroup reductions (every thread gets the result); `red` holds one slot
-// per wavefront and is reused, so each call ends with a barrier.
-__device__ __forceinline__ float block_max(float v, float* red) {
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < kDecWaves; ++i) r = fmaxf(r, red[i]);
-  return r;
+// Inclusive prefix scans over a wavefront with DPP moves (gfx9 wave64): row
+// shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then lane 15 of rows 0
+// and 2 goes to rows 1 and 3, and lane 31 to rows 2 and 3.  Lane i gets the
+// combination of lanes 0..i, lane 63 that of the whole wavefront.  Lanes a
+// move does not reach read 0, the identity of unsigned add and max.  Each
+// step is a register move between lanes, where a shuffle is an LDS
+// crossbar round trip.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
 }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t v) {
+  return ((uint64_t)dpp_move<CTRL, ROWS>((uint32_t)(v >> 32)) << 32) |
+         dpp_move<CTRL, ROWS>((uint32_t)v);
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan(T x, Op op) {
+  x = op(x, dpp_move<0x111, 0xF>(x));   // row_shr:1
+  x = op(x, dpp_move<0x112, 0xF>(x));   // row_shr:2
+  x = op(x, dpp_move<0x114, 0xF>(x));   // row_shr:4
+  x = op(x, dpp_move<0x118, 0xF>(x));   // row_shr:8
+  x = op(x, dpp_move<0x142, 0xA>(x));   // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_move<0x143, 0xC>(x));   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+struct AddOp {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct MaxOp {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+constexpr int kLastLane = kWave - 1;
+
+// Workgroup sum (every thread gets it); `red` holds one slot per wavefront
+// and is reused, so the call ends with a barrier.
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* red) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  v = wave_scan(v, AddOp{});
   __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  if ((threadIdx.x & (kWave - 1)) == kLastLane) red[threadIdx.x / kWave] = v;
   __syncthreads();
   uint64_t r = 0;
   for (int i = 0; i < kDecWaves; ++i) r += red[i];
@@ -130,12 +157,10 @@ __global__ void __launch_bounds__(kDecThreads) ws_select_kernel(const DecidePara
     tmax = max(tmax, key);
     tmin = min(tmin, key);
   }
-  // Largest key and complement of the smallest, reduced together.
-  for (int off = 32; off > 0; off >>= 1) {
-    tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, off, kWave));
-    tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, off, kWave));
-  }
-  if ((tid & (kWave - 1)) == 0) redu[tid / kWave] = ((uint64_t)tmax << 32) | tmin;
+  // Largest key, and the smallest as the largest complement.
+  tmax = wave_scan(tmax, MaxOp{});
+  tmin = ~wave_scan(~tmin, MaxOp{});
+  if ((tid & (kWave - 1)) == kLastLane) redu[tid / kWave] = ((uint64_t)tmax << 32) | tmin;
   __syncthreads();   // also: keys staged
   uint32_t kmax = 0, kmin = 0xffffffffu;
   for (int i = 0; i < kDecWaves; ++i) {
@@ -193,33 +218,31 @@ __global__ void __launch_bounds__(kDecThreads) ws_select_kernel(const DecidePara
         __syncthreads();
       }
       {
-        // Thread t holds bins kPer*t .. kPer*t + kPer-1.  The mass of the
-        // bins above its own: a suffix sum over the threads above,
-        // by shuffles inside each wavefront and the totals of the
-        // wavefronts above.  The one thread whose bins cross T scans them.
+        // Thread t holds the kPer bins from kBins - kPer*(t+1) up, so the
+        // threads before it hold every bin above its own: their mass is a
+        // prefix sum, inside each wavefront by DPP moves, then over the
+        // totals of the wavefronts before.  The one thread whose bins cross
+        // T scans them, highest first.
         constexpr int kPer = kBins / kDecThreads;
+        const int bin0 = kBins - kPer * (tid + 1);
         uint64_t bins[kPer];
         uint64_t sm = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-          bins[j] = hm[kPer * tid + j];
+          bins[j] = hm[bin0 + j];
           sm += bins[j];
         }
         const int lane = tid & (kWave - 1), w = tid / kWave;
-        uint64_t im = sm;
-        for (int off = 1; off < kWave; off <<= 1) {
-          const uint64_t om = __shfl_down(im, off, kWave);
-          if (lane + off < kWave) im += om;
-        }
-        if (lane == 0) wsum[w] = im;
+        const uint64_t im = wave_scan(sm, AddOp{});   // this thread's and those before it
+        if (lane == kLastLane) wsum[w] = im;
         __syncthreads();
         uint64_t run = above + (im - sm);
-        for (int v = w + 1; v < kDecWaves; ++v) run += wsum[v];
+        for (int v = 0; v < w; ++v) run += wsum[v];
         if (run < T && run + sm >= T) {   // exactly one thread holds the bin
 #pragma unroll
           for (int j = kPer - 1; j >= 0; --j) {
             if (run < T && run + bins[j] >= T) {
-              pick_bin = kPer * tid + j;
+              pick_bin = bin0 + j;
               pick_above = run;
             }
             run += bins[j];
@@ -240,8 +263,8 @@ __global__ void __launch_bounds__(kDecThreads) ws_select_kernel(const DecidePara
   uint32_t cnt = 0;
 #pragma unroll 8
   for (int i = tid; i < npg; i += kDecThreads) cnt += key_of(i) >= level_key;
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor((int)cnt, off, kWave);
-  if ((tid & (kWave - 1)) == 0) wsum[tid / kWave] = cnt;
+  cnt = wave_scan(cnt, AddOp{});
+  if ((tid & (kWave - 1)) == kLastLane) wsum[tid / kWave] = cnt;
   __syncthreads();
   uint32_t size = 0;
   for (int i = 0; i < kDecWaves; ++i) size += (uint32_t)wsum[i];
@@ -300,20 +323,17 @@ __global__ void __launch_bounds__(kDecideThreads) decide_kernel(const DecidePara
     }
   }
   // Workgroup sums of the two counts (packed) and minimum candidate.
-  uint64_t counts = ((uint64_t)nf << 32) | ns;
-  for (int off = 32; off > 0; off >>= 1) {
-    counts += __shfl_xor(counts, off, kWave);
-    const uint64_t o = __shfl_xor(best, off, kWave);
-    best = o < best ? o : best;
-  }
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = counts;
+  // (Lane 63 holds each wavefront's; the minimum as the largest complement.)
+  uint64_t counts = wave_scan(((uint64_t)nf << 32) | ns, AddOp{});
+  best = ~wave_scan(~best, MaxOp{});
+  if ((tid & (kWave - 1)) == kLastLane) red[tid / kWave] = counts;
   __syncthreads();
   if (tid == 0) {
     counts = 0;
     for (int i = 0; i < NW; ++i) counts += red[i];
   }
   __syncthreads();
-  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = best;
+  if ((tid & (kWave - 1)) == kLastLane) red[tid / kWave] = best;
   __syncthreads();
   if (tid == 0) {
     for (int i = 0; i < NW; ++i) best = red[i] < best ? red[i] : best;
